@@ -1,0 +1,371 @@
+"""Plain fp64 CPU oracle for the MoBA causal prefill forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP library and imports nothing from it.
+
+Sources (the pages are cited by title and section):
+
+* [wispaper] "MoBA: Learned Block Sparsity for Long-Context Attention"
+  (wispaper.ai review), sections "Starting Point: Exact Softmax Attention and
+  Its Cost", "The Change: Treat KV Blocks as Experts and Route Queries with
+  Top-k Gating" and "Efficiency and Implementation" (Algorithm 1).
+* [glossary] "Mixture of Block Attention (MoBA)" (globaladvisors.biz),
+  section "Underlying computational mechanism" (the text formula
+  MoBA(q,K,V) = Softmax(q K[I]^T) V[I]) and "Mathematical and complexity
+  implications" (at most k*B keys per query).
+* [cn-summary] "MoBA: 面向长上下文大语言模型的混合块注意力机制"
+  (sherconan.github.io), 技术实现 steps 1-4 (block partition, mean-pooled
+  affinity s_i = <q, mean_pool(K[I_i])>, top-k gate, causality rules).
+* [elamur] "MoBA: Mixture of Block Attention for Long-Context LLMs"
+  (research.elamur.ai), "Key points" (causality: future blocks masked out of
+  routing, own block always selected with a causal mask).
+
+What is computed, per sequence s (start a, length L), head h and local query
+position t with own block c = t // B:
+
+1. pool:   kbar_i = mean of K[a+j] over j in [iB, min((i+1)B, L))
+2. gate:   s_i = <Q[a+t], kbar_i> for past blocks i < c (no scale: a positive
+           scale cannot change a ranking)
+3. select: the first min(k-1, c) of 0..c-1 ordered by (-s_i, i); the own block
+           c is added (k counts it); idx = sorted selection, -1 padded to k
+4. tokens: J = union of the selected past blocks' tokens, plus [cB, t]
+5. attend: x_j = scale * <Q[a+t], K[a+j]>, lse = ln sum_{j in J} exp(x_j),
+           o = sum_j exp(x_j - lse) V[a+j]
+
+Blockwise attention followed by an online-softmax merge reaches exactly this
+softmax over J (the merge is an exact identity), so the oracle computes the
+softmax over J directly and never merges.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against hand
+worked examples, library routines (torch SDPA in fp64 for the k >= n and k = 1
+reductions), closed forms and invariants.  The pages print no numeric output
+of the operator itself; the only printed numbers this oracle reproduces are
+the sparsity values of the selection geometry.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Relative gap below which the k-1-th and k-th largest past scores count as a
+# near-tie (selection then is ambiguous at fp32 score precision).
+NEAR_TIE_REL = 1e-5
+
+
+# --------------------------------------------------------------------------
+# geometry
+# --------------------------------------------------------------------------
+
+def sequences(cu_seqlens):
+    """(start, length) of every sequence of a packed batch."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [(int(cu[i]), int(cu[i + 1] - cu[i])) for i in range(len(cu) - 1)]
+
+
+def num_blocks(length, block_size):
+    """Blocks of size B covering L tokens; the last may be partial."""
+    return (length + block_size - 1) // block_size
+
+
+def block_range(i, length, block_size):
+    """Local token range [lo, hi) of block i ([wispaper] "The Change": block
+    partition I_i; 0-based here, partial last block allowed)."""
+    lo = i * block_size
+    return lo, min(lo + block_size, length)
+
+
+# --------------------------------------------------------------------------
+# steps 1-3: pool, gate, select (one sequence, one head)
+# --------------------------------------------------------------------------
+
+def pool_keys_head(K, length, block_size):
+    """Step 1: mean-pooled key of every block of one sequence and head.
+
+    K: [L, d] (any float dtype, converted to fp64 block by block).
+    Returns kbar [n, d] fp64.  [wispaper] "The Change" (mean_pool(K[I_i]));
+    [cn-summary] step 2.
+    """
+    n = num_blocks(length, block_size)
+    d = K.shape[1]
+    kbar = np.zeros((n, d), dtype=np.float64)
+    for i in range(n):
+        lo, hi = block_range(i, length, block_size)
+        kbar[i] = np.asarray(K[lo:hi], dtype=np.float64).mean(axis=0)
+    return kbar
+
+
+def gate_scores_row(q, kbar, c):
+    """Step 2: affinity of query q with every past block i < c."""
+    return np.asarray(kbar[:c], dtype=np.float64) @ np.asarray(q, dtype=np.float64)
+
+
+def select_row(scores, c, topk):
+    """Step 3: causal top-k selection for a query whose own block is c.
+
+    scores: the c past-block scores.  Future blocks are never candidates, the
+    own block is always taken and counts toward k, the remaining k-1 slots go
+    to the highest scores with ties broken toward the lower block index.
+    When c < k-1 there are not enough eligible blocks and the row keeps every
+    block 0..c (masked blocks are never selected to fill slots).
+
+    Returns (idx [topk] int64 ascending, -1 padded; gap; near_tie).
+    gap is s_(k-1) - s_(k) between the (k-1)-th and k-th largest past scores
+    when a k-th candidate exists (c >= k), else +inf.
+    """
+    order = np.lexsort((np.arange(c), -scores))  # primary: -s, secondary: index
+    take = min(topk - 1, c)
+    chosen = sorted(int(i) for i in order[:take]) + [c]
+    idx = np.full(topk, -1, dtype=np.int64)
+    idx[:len(chosen)] = chosen
+    gap, near = np.inf, False
+    if topk >= 2 and c >= topk:
+        a = scores[order[topk - 2]]
+        b = scores[order[topk - 1]]
+        gap = float(a - b)
+        near = bool(gap < NEAR_TIE_REL * max(abs(a), abs(b)))
+    return idx, gap, near
+
+
+def attended_tokens(idx_row, t, block_size):
+    """Step 4: local key positions attended by local query t given its idx row.
+
+    Past blocks contribute all their tokens; the own block contributes
+    [cB, t] (causal mask inside the own block, diagonal included).
+    [wispaper] "The Change" (causality rule); [elamur] "Key points".
+    """
+    c = t // block_size
+    parts = []
+    for i in idx_row:
+        i = int(i)
+        if i < 0:
+            continue
+        if i < c:
+            parts.append(np.arange(i * block_size, (i + 1) * block_size))
+        elif i == c:
+            parts.append(np.arange(c * block_size, t + 1))
+        else:
+            raise ValueError("future block in selection")
+    return np.concatenate(parts)
+
+
+def attend_row(q, K, V, J, scale):
+    """Step 5: exact softmax attention of q over key positions J.
+
+    [glossary] "Underlying computational mechanism": Softmax(q K[I]^T) V[I].
+    Returns (o [d] fp64, lse fp64 natural log).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Kj = np.asarray(K[J], dtype=np.float64)
+    Vj = np.asarray(V[J], dtype=np.float64)
+    x = scale * (Kj @ q)
+    mx = x.max()
+    w = np.exp(x - mx)
+    den = w.sum()
+    lse = mx + np.log(den)
+    o = (w / den) @ Vj
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# whole-batch drivers
+# --------------------------------------------------------------------------
+
+def _rows_by_head(rows, T, H):
+    """rows: None (all) or an int array of (token, head) pairs [R, 2]."""
+    if rows is None:
+        tt, hh = np.meshgrid(np.arange(T), np.arange(H), indexing="ij")
+        return np.stack([tt.ravel(), hh.ravel()], axis=1)
+    return np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+
+
+def _seq_of_token(cu_seqlens, t):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    s = int(np.searchsorted(cu, t, side="right") - 1)
+    return s, int(cu[s]), int(cu[s + 1] - cu[s])
+
+
+def pool_keys(K, cu_seqlens, block_size):
+    """Step 1 over a packed batch: K [T, H, d] -> kbar [NB, H, d] fp64, blocks
+    numbered sequence by sequence (blocks never cross sequences)."""
+    T, H, d = K.shape
+    out = []
+    for a, L in sequences(cu_seqlens):
+        n = num_blocks(L, block_size)
+        kb = np.zeros((n, H, d))
+        for h in range(H):
+            kb[:, h, :] = pool_keys_head(K[a:a + L, h, :], L, block_size)
+        out.append(kb)
+    return np.concatenate(out, axis=0) if out else np.zeros((0, H, d))
+
+
+def moba_reference(Q, K, V, cu_seqlens, block_size, topk, scale, rows=None):
+    """The MoBA forward on (token, head) rows of a packed batch.
+
+    Q, K, V: [T, H, d] arrays (bf16 values held exactly in fp32, or fp32/fp64).
+    rows: None for every row, else [R, 2] (global token, head) pairs.
+    Returns dict with rows, out [R, d], lse [R], idx [R, topk], gap [R],
+    near_tie [R] (bool).
+    """
+    T, H, d = Q.shape
+    rows = _rows_by_head(rows, T, H)
+    R = len(rows)
+    out = np.zeros((R, d))
+    lse = np.zeros(R)
+    idx = np.full((R, topk), -1, dtype=np.int64)
+    gap = np.full(R, np.inf)
+    near = np.zeros(R, dtype=bool)
+    kbar_cache = {}
+    for r, (t, h) in enumerate(rows):
+        s, a, L = _seq_of_token(cu_seqlens, int(t))
+        key = (s, int(h))
+        if key not in kbar_cache:
+            kbar_cache[key] = pool_keys_head(K[a:a + L, h, :], L, block_size)
+        kbar = kbar_cache[key]
+        tl = int(t) - a
+        c = tl // block_size
+        sc = gate_scores_row(Q[t, h, :], kbar, c)
+        idx[r], gap[r], near[r] = select_row(sc, c, topk)
+        J = attended_tokens(idx[r], tl, block_size)
+        out[r], lse[r] = attend_row(Q[t, h, :], K[a:a + L, h, :], V[a:a + L, h, :], J, scale)
+    return dict(rows=rows, out=out, lse=lse, idx=idx, gap=gap, near_tie=near)
+
+
+def gate_reference(Q, K, cu_seqlens, block_size, topk, rows=None):
+    """Steps 1-3 only (block selection), vectorised per sequence and head:
+    one fp64 matrix product of the queries with the pooled keys, then the
+    per-row causal top-k of ``select_row``."""
+    T, H, d = Q.shape
+    rows = _rows_by_head(rows, T, H)
+    R = len(rows)
+    idx = np.full((R, topk), -1, dtype=np.int64)
+    gap = np.full(R, np.inf)
+    near = np.zeros(R, dtype=bool)
+    order = np.lexsort((rows[:, 0], rows[:, 1]))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    seq_of = np.searchsorted(cu, rows[:, 0], side="right") - 1
+    groups = {}
+    for r in order:
+        groups.setdefault((int(seq_of[r]), int(rows[r, 1])), []).append(r)
+    for (s, h), rs in groups.items():
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        kbar = pool_keys_head(K[a:a + L, h, :], L, block_size)
+        rs = np.asarray(rs)
+        tl = rows[rs, 0] - a
+        S = np.asarray(Q[rows[rs, 0], h, :], dtype=np.float64) @ kbar.T
+        for j, r in enumerate(rs):
+            c = int(tl[j]) // block_size
+            idx[r], gap[r], near[r] = select_row(S[j, :c], c, topk)
+    return dict(rows=rows, idx=idx, gap=gap, near_tie=near)
+
+
+def attend_given_selection(Q, K, V, cu_seqlens, block_size, idx, scale, rows):
+    """Steps 4-5 for given (token, head) rows and a given selection per row.
+
+    Used for rows whose selection is ambiguous (near-ties): the selection to
+    use is checked for validity first by ``selection_is_valid``.
+    """
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    R = len(rows)
+    d = Q.shape[2]
+    out = np.zeros((R, d))
+    lse = np.zeros(R)
+    for r, (t, h) in enumerate(rows):
+        s, a, L = _seq_of_token(cu_seqlens, int(t))
+        J = attended_tokens(idx[r], int(t) - a, block_size)
+        out[r], lse[r] = attend_row(Q[t, h, :], K[a:a + L, h, :], V[a:a + L, h, :], J, scale)
+    return out, lse
+
+
+def selection_is_valid(Q, K, cu_seqlens, block_size, topk, row, idx_row,
+                       rel=NEAR_TIE_REL):
+    """Whether idx_row is a correct causal top-k for (token, head) ``row`` up
+    to score differences below ``rel`` relative: ascending, own block last,
+    no future block, the right count, and no unselected past block scoring
+    higher than a selected one by more than the tolerance."""
+    t, h = int(row[0]), int(row[1])
+    s, a, L = _seq_of_token(cu_seqlens, t)
+    tl = t - a
+    c = tl // block_size
+    idx_row = [int(x) for x in idx_row]
+    valid = [x for x in idx_row if x >= 0]
+    if idx_row[len(valid):] != [-1] * (topk - len(valid)):
+        return False
+    if valid != sorted(set(valid)) or not valid or valid[-1] != c:
+        return False
+    past = valid[:-1]
+    if len(past) != min(topk - 1, c) or any(x < 0 or x >= c for x in past):
+        return False
+    if not past:
+        return True
+    kbar = pool_keys_head(K[a:a + L, h, :], L, block_size)
+    sc = gate_scores_row(Q[t, h, :], kbar, c)
+    worst_in = min(sc[x] for x in past)
+    others = [sc[i] for i in range(c) if i not in past]
+    if not others:
+        return True
+    best_out = max(others)
+    return bool(best_out - worst_in <= rel * max(abs(best_out), abs(worst_in)))
+
+
+# --------------------------------------------------------------------------
+# second, independent formulation and the dense baseline
+# --------------------------------------------------------------------------
+
+def brute_force_mask(cu_seqlens, block_size, idx):
+    """Token-level mask M[t, j] = [block(j) selected by t] and [j <= t] and
+    [same sequence], built from per-row selections idx [T, topk] (one head).
+
+    [glossary] "Mathematical and complexity implications": the learned block
+    mask over the N x N score matrix.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    M = np.zeros((T, T), dtype=bool)
+    for a, L in sequences(cu):
+        for tl in range(L):
+            sel = {int(x) for x in idx[a + tl] if x >= 0}
+            for jl in range(tl + 1):
+                if jl // block_size in sel:
+                    M[a + tl, a + jl] = True
+    return M
+
+
+def masked_softmax_attention(Q, K, V, M, scale):
+    """Dense softmax over the allowed positions of mask M (one head):
+    Q, K, V [T, d]; returns out [T, d], lse [T]."""
+    X = scale * (np.asarray(Q, np.float64) @ np.asarray(K, np.float64).T)
+    X = np.where(M, X, -np.inf)
+    mx = X.max(axis=1, keepdims=True)
+    W = np.exp(X - mx)
+    den = W.sum(axis=1, keepdims=True)
+    out = (W / den) @ np.asarray(V, np.float64)
+    lse = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+def dense_causal_reference(Q, K, V, cu_seqlens, scale, rows=None):
+    """Full causal softmax attention per sequence (the exact baseline of
+    [wispaper] "Starting Point"), on (token, head) rows."""
+    T, H, d = Q.shape
+    rows = _rows_by_head(rows, T, H)
+    out = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for r, (t, h) in enumerate(rows):
+        s, a, L = _seq_of_token(cu_seqlens, int(t))
+        J = np.arange(0, int(t) - a + 1)
+        out[r], lse[r] = attend_row(Q[t, h, :], K[a:a + L, h, :], V[a:a + L, h, :], J, scale)
+    return out, lse
+
+
+def sparsity(seq_len, block_size, topk, seed=0):
+    """Fraction of the seq_len positions that the last query of a sequence
+    does not attend to, through the oracle's own selection on random scores
+    ([wispaper] "The Change", the sparsity paragraph: 1 - k*B/N when N is a
+    multiple of B; the count does not depend on which blocks win)."""
+    last = seq_len - 1
+    c = last // block_size
+    scores = np.random.default_rng(seed).standard_normal(c)
+    idx, _, _ = select_row(scores, c, topk)
+    J = attended_tokens(idx, last, block_size)
+    return 1.0 - len(J) / seq_len
