@@ -1,0 +1,301 @@
+// C ABI of libmoba.so: host-side validation, workspace carve-up and launch
+// order.  See include/moba.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/moba.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+moba_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MOBA_ERR_HIP;
+}
+
+bool dtype_ok(int dt) { return dt == MOBA_F32 || dt == MOBA_BF16; }
+
+// Checks of the shared geometry arguments.  Nothing here touches the device.
+moba_status check_geometry(int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                           int num_seqs, int total_tokens, int max_seqlen, int total_blocks,
+                           int num_heads, int head_dim, int block_size) {
+  if (!cu_seqlens || !cu_blocks) return MOBA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOBA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || total_tokens < 0 || max_seqlen < 0 || total_blocks < 0)
+    return MOBA_ERR_INVALID_ARG;
+  if (num_heads < 1 || head_dim < 1 || block_size < 1) return MOBA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
+  if (block_size % 64 != 0) return MOBA_ERR_UNSUPPORTED;
+  if (max_seqlen > total_tokens) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens > 0) {
+    if (max_seqlen < 1) return MOBA_ERR_INVALID_ARG;
+    if ((long long)max_seqlen * num_seqs < total_tokens) return MOBA_ERR_INVALID_ARG;
+    const long long min_blocks = ((long long)total_tokens + block_size - 1) / block_size;
+    if (total_blocks < min_blocks || total_blocks > total_tokens) return MOBA_ERR_INVALID_ARG;
+    if (total_blocks < (max_seqlen + block_size - 1) / block_size) return MOBA_ERR_INVALID_ARG;
+  } else if (total_blocks != 0) {
+    return MOBA_ERR_INVALID_ARG;
+  }
+  // 32-bit limits of the launch grids and of the packed list entries
+  if ((long long)num_heads * total_blocks + 1 >= (1LL << 31)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)total_blocks * (block_size / 64) >= (1LL << 31)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)num_seqs * ((max_seqlen + 63) / 64) >= (1LL << 31)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)total_tokens * num_heads >= (1LL << 33)) return MOBA_ERR_UNSUPPORTED;
+  if (num_heads > 65535) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+moba_status check_topk(int total_tokens, int topk) {
+  if (topk < 1) return MOBA_ERR_INVALID_ARG;
+  if (topk > 64) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)total_tokens * topk >= (1LL << 31)) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+moba::Geo make_geo(const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                   int total_tokens, int max_seqlen, int total_blocks, int num_heads,
+                   int head_dim, int block_size) {
+  moba::Geo g;
+  g.cu_seqlens = cu_seqlens;
+  g.cu_blocks = cu_blocks;
+  g.num_seqs = num_seqs;
+  g.total_tokens = total_tokens;
+  g.max_seqlen = max_seqlen;
+  g.total_blocks = total_blocks;
+  g.num_heads = num_heads;
+  g.head_dim = head_dim;
+  g.block_size = block_size;
+  return g;
+}
+
+long long hist_entries_bound(const moba::Geo& g, int topk) {
+  return (long long)g.total_tokens * g.num_heads * (topk - 1);
+}
+
+long long hist_tiles_bound(const moba::Geo& g, int topk) {
+  if (topk < 2) return 0;
+  const long long e = hist_entries_bound(g, topk);
+  return (e + moba::kMfmaTileQ - 1) / moba::kMfmaTileQ + (long long)g.num_heads * g.total_blocks;
+}
+
+}  // namespace
+
+namespace moba {
+
+AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long long H,
+                                    long long D, long long B, long long topk) {
+  AttnWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t nkeys = (size_t)(H * NB);
+  w.counts = take(nkeys * 4);
+  w.offsets = take((nkeys + 1) * 4);
+  w.tile_offsets = take((nkeys + 1) * 4);
+  w.list = take((size_t)(T * H * (topk > 1 ? topk - 1 : 1)) * 4);
+  w.lse_part = take((size_t)(T * H * topk) * 4);
+  w.o_part = take((size_t)(T * H * topk * D) * (bf16 ? 2 : 4));
+  w.vt = take(bf16 ? (size_t)(NB * B * H * D) * 2 : 0);
+  w.total = off;
+  return w;
+}
+
+size_t dense_workspace_bytes(bool bf16, long long NB, long long H, long long D, long long B) {
+  return align_up(bf16 ? (size_t)(NB * B * H * D) * 2 : 0) + kAlign;
+}
+
+}  // namespace moba
+
+extern "C" {
+
+int moba_api_version(void) { return MOBA_API_VERSION; }
+
+const char* moba_status_str(int status) {
+  switch (status) {
+    case MOBA_OK: return "MOBA_OK";
+    case MOBA_ERR_INVALID_ARG: return "MOBA_ERR_INVALID_ARG";
+    case MOBA_ERR_UNSUPPORTED: return "MOBA_ERR_UNSUPPORTED";
+    case MOBA_ERR_WORKSPACE_TOO_SMALL: return "MOBA_ERR_WORKSPACE_TOO_SMALL";
+    case MOBA_ERR_HIP: return "MOBA_ERR_HIP";
+    default: return "MOBA_ERR_UNKNOWN";
+  }
+}
+
+int moba_last_hip_error(void) { return g_last_hip_error; }
+
+moba_status moba_pool_keys(const void* k, int dtype, const int32_t* cu_seqlens,
+                           const int32_t* cu_blocks, int num_seqs, int total_tokens,
+                           int max_seqlen, int total_blocks, int num_heads, int head_dim,
+                           int block_size, float* kbar, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!k || !kbar) return MOBA_ERR_INVALID_ARG;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  hipError_t e = moba::launch_pool_keys(k, dtype == MOBA_BF16, g, kbar, (hipStream_t)stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
+moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
+                           const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                           int total_tokens, int max_seqlen, int total_blocks, int num_heads,
+                           int head_dim, int block_size, int topk, int32_t* block_idx,
+                           void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !kbar || !block_idx) return MOBA_ERR_INVALID_ARG;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  hipError_t e = moba::launch_gate_topk(q, dtype == MOBA_BF16, kbar, g, topk, block_idx,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
+size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks, int num_heads,
+                                 int head_dim, int block_size, int topk) {
+  if (!dtype_ok(dtype) || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||
+      (head_dim != 64 && head_dim != 128) || block_size < 64 || block_size % 64 != 0 ||
+      check_topk(total_tokens, topk) != MOBA_OK)
+    return 0;
+  return moba::attn_workspace_layout(dtype == MOBA_BF16, total_tokens, total_blocks, num_heads,
+                                     head_dim, block_size, topk)
+      .total + kAlign;
+}
+
+moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                          int total_tokens, int max_seqlen, int total_blocks, int num_heads,
+                          int head_dim, int block_size, int topk, const int32_t* block_idx,
+                          float softmax_scale, void* out, int out_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (!dtype_ok(out_dtype)) return MOBA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !k || !v || !block_idx || !out || !lse || !workspace) return MOBA_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace % kAlign != 0) return MOBA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == MOBA_BF16;
+  const moba::AttnWorkspace L = moba::attn_workspace_layout(
+      bf16, total_tokens, total_blocks, num_heads, head_dim, block_size, topk);
+  if (workspace_bytes < L.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  const long long tiles = hist_tiles_bound(g, topk);
+  if (tiles >= (1LL << 31) || hist_entries_bound(g, topk) / 4 >= (1LL << 31))
+    return MOBA_ERR_UNSUPPORTED;
+
+  char* ws = (char*)workspace;
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* tile_offsets = (int32_t*)(ws + L.tile_offsets);
+  int32_t* list = (int32_t*)(ws + L.list);
+  float* lse_part = (float*)(ws + L.lse_part);
+  void* o_part = ws + L.o_part;
+  hipStream_t s = (hipStream_t)stream;
+  const bool out_bf16 = out_dtype == MOBA_BF16;
+  hipError_t e;
+
+  if (bf16) {
+    uint16_t* vt = (uint16_t*)(ws + L.vt);
+    if ((e = moba::launch_v_transpose(v, g, vt, s)) != hipSuccess) return hip_fail(e);
+    if ((e = moba::launch_bucket(block_idx, g, topk, moba::kMfmaTileQ, counts, offsets,
+                                 tile_offsets, list, s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list, offsets,
+                                         tile_offsets, tiles, (uint16_t*)o_part, lse_part,
+                                         s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale, (uint16_t*)o_part,
+                                        lse_part, s)) != hipSuccess)
+      return hip_fail(e);
+  } else {
+    if ((e = moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
+                                 tile_offsets, list, s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = moba::launch_attn_f32_hist((const float*)q, (const float*)k, (const float*)v, g,
+                                        topk, softmax_scale, list, offsets,
+                                        hist_entries_bound(g, topk), (float*)o_part, lse_part,
+                                        s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = moba::launch_attn_f32_own((const float*)q, (const float*)k, (const float*)v, g,
+                                       topk, softmax_scale, (float*)o_part, lse_part, s)) !=
+        hipSuccess)
+      return hip_fail(e);
+  }
+  if ((e = moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, out, out_bf16, lse,
+                              s)) != hipSuccess)
+    return hip_fail(e);
+  return MOBA_OK;
+}
+
+size_t moba_dense_workspace_bytes(int dtype, int total_tokens, int total_blocks, int num_heads,
+                                  int head_dim, int block_size) {
+  if (!dtype_ok(dtype) || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||
+      (head_dim != 64 && head_dim != 128) || block_size < 64 || block_size % 64 != 0)
+    return 0;
+  return moba::dense_workspace_bytes(dtype == MOBA_BF16, total_blocks, num_heads, head_dim,
+                                     block_size);
+}
+
+moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, int dtype,
+                                  const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                  int num_seqs, int total_tokens, int max_seqlen,
+                                  int total_blocks, int num_heads, int head_dim,
+                                  int block_size, float softmax_scale, void* out,
+                                  int out_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  if (!dtype_ok(out_dtype)) return MOBA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !k || !v || !out || !lse) return MOBA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == MOBA_BF16;
+  const size_t need = moba::dense_workspace_bytes(bf16, total_blocks, num_heads, head_dim,
+                                                  block_size) - kAlign;
+  if (need > 0) {
+    if (!workspace) return MOBA_ERR_INVALID_ARG;
+    if ((uintptr_t)workspace % kAlign != 0) return MOBA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (bf16) {
+    uint16_t* vt = (uint16_t*)workspace;
+    if ((e = moba::launch_v_transpose(v, g, vt, s)) != hipSuccess) return hip_fail(e);
+    if ((e = moba::launch_attn_mfma_dense(q, k, vt, g, softmax_scale, out,
+                                          out_dtype == MOBA_BF16, lse, s)) != hipSuccess)
+      return hip_fail(e);
+  } else {
+    if ((e = moba::launch_attn_f32_dense((const float*)q, (const float*)k, (const float*)v, g,
+                                         softmax_scale, out, out_dtype == MOBA_BF16, lse, s)) !=
+        hipSuccess)
+      return hip_fail(e);
+  }
+  return MOBA_OK;
+}
+
+}  // extern "C"

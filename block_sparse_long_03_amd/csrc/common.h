@@ -1,0 +1,91 @@
+// Shared device helpers for the MoBA gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 <-> fp32.  bf16 -> fp32 is exact (the bf16 bits are the high half).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts natively).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Index of the sequence that owns global block `gb` (largest s with
+// cu_blocks[s] <= gb).  cu_blocks is non-decreasing with num_seqs + 1 entries.
+__device__ __forceinline__ int seq_of_block(const int32_t* __restrict__ cu_blocks,
+                                            int num_seqs, int gb) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_blocks[mid] <= gb) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Largest i in [0, n) with arr[i] <= x for a non-decreasing arr (arr[0] <= x).
+__device__ __forceinline__ int upper_index(const int32_t* __restrict__ arr, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (arr[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Length of sequence s clamped to the packed batch.
+__device__ __forceinline__ void seq_span(const int32_t* __restrict__ cu_seqlens, int s,
+                                         int total_tokens, int* start, int* len) {
+  int a = cu_seqlens[s];
+  int b = cu_seqlens[s + 1];
+  a = min(max(a, 0), total_tokens);
+  b = min(max(b, a), total_tokens);
+  *start = a;
+  *len = b - a;
+}
+
+// Walks a block_idx row and reports, for each entry, whether it is a
+// historical selection (0 <= e < c and larger than the previous accepted
+// entry).  Accepted historical entries get consecutive slots 0, 1, ...; the
+// own block always uses slot topk - 1.  Both the bucketing and the merge
+// apply exactly this rule.
+__device__ __forceinline__ int count_hist(const int32_t* __restrict__ row, int topk, int c) {
+  int nh = 0, last = -1;
+  for (int j = 0; j < topk; ++j) {
+    int e = row[j];
+    if (e >= 0 && e < c && e > last) { ++nh; last = e; }
+  }
+  return nh;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace moba

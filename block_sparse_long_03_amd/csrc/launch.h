@@ -1,0 +1,83 @@
+// Host-side launch wrappers shared between the kernel translation units and
+// the C ABI layer.  All pointers are device pointers; nothing here allocates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moba {
+
+struct Geo {
+  const int32_t* cu_seqlens;
+  const int32_t* cu_blocks;
+  int num_seqs;
+  int total_tokens;
+  int max_seqlen;
+  int total_blocks;
+  int num_heads;
+  int head_dim;
+  int block_size;
+};
+
+// Query tile (rows per workgroup) of the bf16 MFMA attention kernels and of
+// the fp32 attention kernels; the bucket scan cuts the per-block query lists
+// into tiles of this many rows.
+constexpr int kMfmaTileQ = 128;
+constexpr int kF32TileQ = 1;
+
+// Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
+struct AttnWorkspace {
+  size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, total;
+};
+AttnWorkspace attn_workspace_layout(bool bf16, long long total_tokens, long long total_blocks,
+                                    long long num_heads, long long head_dim,
+                                    long long block_size, long long topk);
+size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_heads,
+                             long long head_dim, long long block_size);
+
+hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar, hipStream_t st);
+hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const Geo& g,
+                            int topk, int32_t* block_idx, hipStream_t st);
+
+// Query bucketing: counts per (head, KV block), exclusive scans of entries and
+// of tiles, and the scatter of (token, slot) entries into per-block lists.
+hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
+                         int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                         int32_t* list, hipStream_t st);
+
+// Transposed, key-permuted copy of V per (block, head) for the MFMA kernels.
+hipError_t launch_v_transpose(const void* v, const Geo& g, uint16_t* vt, hipStream_t st);
+
+// bf16 MFMA attention.  mode: 0 historical blocks (gathered queries, partials),
+// 1 own block (causal, partials), 2 dense causal (final output).
+hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* vt,
+                                 const Geo& g, int topk, float scale, const int32_t* list,
+                                 const int32_t* offsets, const int32_t* tile_offsets,
+                                 long long max_tiles, uint16_t* o_part, float* lse_part,
+                                 hipStream_t st);
+hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt,
+                                const Geo& g, int topk, float scale, uint16_t* o_part,
+                                float* lse_part, hipStream_t st);
+hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
+                                  const Geo& g, float scale, void* out, bool out_bf16,
+                                  float* lse, hipStream_t st);
+
+// fp32 VALU attention (one wave per query row and key range).
+hipError_t launch_attn_f32_hist(const float* q, const float* k, const float* v, const Geo& g,
+                                int topk, float scale, const int32_t* list,
+                                const int32_t* offsets, long long max_entries, float* o_part,
+                                float* lse_part, hipStream_t st);
+hipError_t launch_attn_f32_own(const float* q, const float* k, const float* v, const Geo& g,
+                               int topk, float scale, float* o_part, float* lse_part,
+                               hipStream_t st);
+hipError_t launch_attn_f32_dense(const float* q, const float* k, const float* v, const Geo& g,
+                                 float scale, void* out, bool out_bf16, float* lse,
+                                 hipStream_t st);
+
+// Online-softmax combine of the partials of every (token, head) row.
+hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
+                        bool part_bf16, const float* lse_part, void* out, bool out_bf16,
+                        float* lse, hipStream_t st);
+
+}  // namespace moba

@@ -1,0 +1,229 @@
+"""Python binding of libmoba.so (ctypes).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream, every computation runs in the library's HIP kernels.  The entry points
+carry the C names of ``include/moba.h``; ``forward`` and ``dense`` chain them.
+
+Loading fails loudly when the library has not been built (there is no
+fallback of any kind).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoba.so")
+
+MOBA_OK = 0
+MOBA_ERR_INVALID_ARG = -1
+MOBA_ERR_UNSUPPORTED = -2
+MOBA_ERR_WORKSPACE_TOO_SMALL = -3
+MOBA_ERR_HIP = -4
+MOBA_F32 = 0
+MOBA_BF16 = 1
+
+EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
+           "moba_gate_topk", "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_dense_workspace_bytes", "moba_dense_causal_fwd"]
+
+_lib = None
+
+
+class MobaError(RuntimeError):
+    def __init__(self, fn, status, hip_error=0):
+        self.status = status
+        self.hip_error = hip_error
+        name = lib().moba_status_str(status).decode()
+        extra = f" (hip error {hip_error})" if status == MOBA_ERR_HIP else ""
+        super().__init__(f"{fn} failed: {name}{extra}")
+
+
+def lib():
+    """Loads libmoba.so once (after torch, so that both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_long_03_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    geo = [vp, vp, i32, i32, i32, i32, i32, i32, i32]  # cu_seqlens .. block_size
+    L.moba_api_version.restype = i32
+    L.moba_api_version.argtypes = []
+    L.moba_status_str.restype = ctypes.c_char_p
+    L.moba_status_str.argtypes = [i32]
+    L.moba_last_hip_error.restype = i32
+    L.moba_last_hip_error.argtypes = []
+    L.moba_pool_keys.restype = i32
+    L.moba_pool_keys.argtypes = [vp, i32] + geo + [vp, vp]
+    L.moba_gate_topk.restype = i32
+    L.moba_gate_topk.argtypes = [vp, i32, vp] + geo + [i32, vp, vp]
+    L.moba_attn_workspace_bytes.restype = sz
+    L.moba_attn_workspace_bytes.argtypes = [i32] * 7
+    L.moba_attn_fwd.restype = i32
+    L.moba_attn_fwd.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, vp, sz, vp]
+    L.moba_dense_workspace_bytes.restype = sz
+    L.moba_dense_workspace_bytes.argtypes = [i32] * 6
+    L.moba_dense_causal_fwd.restype = i32
+    L.moba_dense_causal_fwd.argtypes = [vp, vp, vp, i32] + geo + [f32, vp, i32, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != MOBA_OK:
+        raise MobaError(fn, status, lib().moba_last_hip_error())
+
+
+def _dtype_code(t):
+    if t == torch.bfloat16:
+        return MOBA_BF16
+    if t == torch.float32:
+        return MOBA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Geometry:
+    """Packed-batch geometry: host scalars plus the device cu_seqlens / cu_blocks."""
+    cu_seqlens: torch.Tensor  # int32 [S+1] on the device
+    cu_blocks: torch.Tensor   # int32 [S+1] on the device
+    num_seqs: int
+    total_tokens: int
+    max_seqlen: int
+    total_blocks: int
+    block_size: int
+
+    @staticmethod
+    def make(seqlens_or_cu, block_size, device, is_cu=True):
+        cu = [int(x) for x in seqlens_or_cu]
+        if not is_cu:
+            acc = [0]
+            for L in cu:
+                acc.append(acc[-1] + L)
+            cu = acc
+        lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+        cb = [0]
+        for L in lens:
+            cb.append(cb[-1] + (L + block_size - 1) // block_size)
+        dev = torch.device(device)
+        return Geometry(torch.tensor(cu, dtype=torch.int32, device=dev),
+                        torch.tensor(cb, dtype=torch.int32, device=dev),
+                        len(lens), cu[-1], max(lens) if lens else 0, cb[-1], block_size)
+
+    def args(self, num_heads, head_dim):
+        return [_ptr(self.cu_seqlens), _ptr(self.cu_blocks), self.num_seqs, self.total_tokens,
+                self.max_seqlen, self.total_blocks, num_heads, head_dim, self.block_size]
+
+
+def _qkv_shape(x, geom):
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("expected a contiguous [T, H, d] tensor")
+    if x.shape[0] != geom.total_tokens:
+        raise ValueError("token count does not match the geometry")
+    return x.shape[1], x.shape[2]
+
+
+def moba_pool_keys(k, geom, kbar=None, stream=None):
+    H, d = _qkv_shape(k, geom)
+    if kbar is None:
+        kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=k.device)
+    _check("moba_pool_keys", lib().moba_pool_keys(
+        _ptr(k), _dtype_code(k.dtype), *geom.args(H, d), _ptr(kbar), _stream(stream)))
+    return kbar
+
+
+def moba_gate_topk(q, kbar, geom, topk, block_idx=None, stream=None):
+    H, d = _qkv_shape(q, geom)
+    if block_idx is None:
+        block_idx = torch.empty((geom.total_tokens, H, topk), dtype=torch.int32, device=q.device)
+    _check("moba_gate_topk", lib().moba_gate_topk(
+        _ptr(q), _dtype_code(q.dtype), _ptr(kbar), *geom.args(H, d), int(topk),
+        _ptr(block_idx), _stream(stream)))
+    return block_idx
+
+
+def moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
+                              block_size, topk):
+    return int(lib().moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
+                                               head_dim, block_size, topk))
+
+
+def moba_dense_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
+                               block_size):
+    return int(lib().moba_dense_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
+                                                head_dim, block_size))
+
+
+def _workspace(nbytes, device):
+    # torch allocations are at least 256-byte aligned
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moba_attn_fwd(q, k, v, geom, topk, block_idx, scale, out=None, out_dtype=None, lse=None,
+                  workspace=None, stream=None):
+    H, d = _qkv_shape(q, geom)
+    dt = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(moba_attn_workspace_bytes(
+            dt, geom.total_tokens, geom.total_blocks, H, d, geom.block_size, topk), q.device)
+    _check("moba_attn_fwd", lib().moba_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), dt, *geom.args(H, d), int(topk), _ptr(block_idx),
+        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def moba_dense_causal_fwd(q, k, v, geom, scale, out=None, out_dtype=None, lse=None,
+                          workspace=None, stream=None):
+    H, d = _qkv_shape(q, geom)
+    dt = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(moba_dense_workspace_bytes(
+            dt, geom.total_tokens, geom.total_blocks, H, d, geom.block_size), q.device)
+    _check("moba_dense_causal_fwd", lib().moba_dense_causal_fwd(
+        _ptr(q), _ptr(k), _ptr(v), dt, *geom.args(H, d), float(scale), _ptr(out),
+        _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out, lse
+
+
+def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):
+    """MoBA prefill forward: pool -> gate/top-k -> sparse attention.
+    Returns (out, lse, block_idx)."""
+    kbar = moba_pool_keys(k, geom, stream=stream)
+    idx = moba_gate_topk(q, kbar, geom, topk, stream=stream)
+    out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
+                             workspace=workspace, stream=stream)
+    return out, lse, idx
+
+
+def dense(q, k, v, geom, scale, out_dtype=None, workspace=None, stream=None):
+    """Dense causal attention with the library's own kernel.  Returns (out, lse)."""
+    return moba_dense_causal_fwd(q, k, v, geom, scale, out_dtype=out_dtype,
+                                 workspace=workspace, stream=stream)

@@ -1,0 +1,186 @@
+/*
+ * moba.h - C ABI of libmoba.so: MoBA (Mixture of Block Attention) causal
+ * prefill forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (cited by page title and section):
+ *   "MoBA: Learned Block Sparsity for Long-Context Attention" (wispaper.ai
+ *   review), section "The Change: Treat KV Blocks as Experts and Route Queries
+ *   with Top-k Gating": K/V are split into blocks of B tokens, each block's
+ *   keys are mean-pooled, a query scores each block by its inner product with
+ *   the pooled key, keeps the top-k blocks, never selects a future block,
+ *   always selects its own block (with a causal mask inside it), and runs
+ *   exact softmax attention over the selected blocks' tokens.  Section
+ *   "Efficiency and Implementation" (Algorithm 1): queries are arranged by the
+ *   KV blocks they selected, own-block and historical-block attention are
+ *   computed separately and combined with an online softmax.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense row-major and live in device memory owned by the
+ *     caller: q, k, v, out are [total_tokens, num_heads, head_dim]; lse is
+ *     [total_tokens, num_heads]; kbar is [total_blocks, num_heads, head_dim];
+ *     block_idx is [total_tokens, num_heads, topk].
+ *   - Variable-length batches are packed: sequence s owns tokens
+ *     [cu_seqlens[s], cu_seqlens[s+1]) and blocks [cu_blocks[s],
+ *     cu_blocks[s+1]) with cu_blocks[s+1] - cu_blocks[s] = ceil(L_s / B).
+ *     Blocks never cross sequences; block ids inside block_idx are local to
+ *     the sequence and 0-based.  The last block of a sequence may be partial.
+ *     cu_seqlens and cu_blocks are device int32 arrays of num_seqs + 1
+ *     entries.  The host passes the matching scalars (total_tokens,
+ *     max_seqlen = max L_s, total_blocks = cu_blocks[num_seqs]) so that no
+ *     call reads device memory from the host; they must agree with the
+ *     arrays (the kernels clamp every index, so a mismatch gives wrong
+ *     numbers, not out-of-bounds accesses of q/k/v).
+ *   - dtype (moba_dtype) is the element type of q, k, v: MOBA_BF16 (the
+ *     production path: bf16 MFMA, fp32 accumulation) or MOBA_F32 (fp32 VALU
+ *     path for small, high-precision checks).
+ *   - Supported: head_dim 64 or 128; block_size a positive multiple of 64;
+ *     1 <= topk <= 64; total_tokens * topk < 2^31.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream), allocates no device memory and keeps no state between
+ *     calls.  Arguments are validated on the host before anything is
+ *     launched; an invalid call launches nothing and returns an error.
+ *   - Errors: MOBA_OK (0) or a negative moba_status.  MOBA_ERR_HIP means a
+ *     launch failed; moba_last_hip_error() returns that HIP error code
+ *     (per calling thread).  The library never prints or aborts.
+ */
+#ifndef MOBA_H_
+#define MOBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_API_VERSION 1
+
+typedef enum moba_status {
+  MOBA_OK = 0,
+  MOBA_ERR_INVALID_ARG = -1,         /* null pointer, negative size, inconsistent geometry */
+  MOBA_ERR_UNSUPPORTED = -2,         /* valid but outside the supported shapes or dtypes */
+  MOBA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes below the required size */
+  MOBA_ERR_HIP = -4                  /* a HIP launch failed, see moba_last_hip_error() */
+} moba_status;
+
+typedef enum moba_dtype {
+  MOBA_F32 = 0,
+  MOBA_BF16 = 1
+} moba_dtype;
+
+/* Library ABI version (MOBA_API_VERSION of the build). */
+int moba_api_version(void);
+
+/* Human-readable name of a moba_status; never NULL. */
+const char* moba_status_str(int status);
+
+/* HIP error code (hipError_t as int) of the last MOBA_ERR_HIP on this thread. */
+int moba_last_hip_error(void);
+
+/*
+ * Block mean-pool of the keys.
+ *   kbar[b, h, :] = mean of k[t, h, :] over the tokens t of block b (a partial
+ *   last block averages the tokens it has).
+ * Defined by the mean_pool(K[I_i]) of the affinity in "MoBA: Learned Block
+ * Sparsity for Long-Context Attention", section "The Change", and step 2 of
+ * "MoBA: 面向长上下文大语言模型的混合块注意力机制" (技术实现).
+ *   k     [total_tokens, num_heads, head_dim], dtype
+ *   kbar  [total_blocks, num_heads, head_dim] fp32, written in full
+ * Summation is fp32 in a fixed order (deterministic).
+ */
+moba_status moba_pool_keys(const void* k, int dtype,
+                           const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                           int num_seqs, int total_tokens, int max_seqlen,
+                           int total_blocks, int num_heads, int head_dim,
+                           int block_size, float* kbar, void* stream);
+
+/*
+ * Gate and causal top-k selection.
+ * For query token t (local position p, own block c = p / B) and head h:
+ *   s_i = <q[t, h, :], kbar[block i, h, :]> for past blocks i < c only
+ *   (future blocks are masked out of routing); the own block c is always
+ *   selected and counts toward topk; the remaining topk - 1 slots take the
+ *   highest s_i, ties going to the lower block index; rows with c < topk - 1
+ *   select every block 0..c.
+ * "MoBA: Learned Block Sparsity for Long-Context Attention", section "The
+ * Change" (affinity, hard top-k gate, causality rules).
+ *   q          [total_tokens, num_heads, head_dim], dtype
+ *   kbar       output of moba_pool_keys
+ *   block_idx  [total_tokens, num_heads, topk] int32, written in full: the
+ *              selected local block ids in ascending order (so the own block
+ *              is the last valid entry), then -1 padding
+ * Scores are fp32 (fp32 products of the exact inputs, fp32 accumulation).
+ */
+moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
+                           const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                           int num_seqs, int total_tokens, int max_seqlen,
+                           int total_blocks, int num_heads, int head_dim,
+                           int block_size, int topk, int32_t* block_idx,
+                           void* stream);
+
+/*
+ * Workspace bytes moba_attn_fwd needs for this geometry (0 when the
+ * arguments are invalid).  The workspace holds the per-(KV block, head)
+ * query lists, the per-(query, selected block) partial results and a
+ * transposed copy of V.
+ */
+size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks,
+                                 int num_heads, int head_dim, int block_size,
+                                 int topk);
+
+/*
+ * Sparse attention over the selected blocks.
+ *   out[t, h, :] = sum_{j in J} softmax_j(scale * <q[t,h], k[j,h]>) v[j, h, :]
+ *   lse[t, h]    = ln sum_{j in J} exp(scale * <q[t,h], k[j,h]>)
+ * where J is the union of the tokens of the historical blocks listed in
+ * block_idx[t, h, :] and the own-block tokens up to and including t.
+ * "Mixture of Block Attention (MoBA)" (globaladvisors.biz), "Underlying
+ * computational mechanism" (Softmax(q K[I]^T) V[I]); "MoBA: Learned Block
+ * Sparsity for Long-Context Attention", "Efficiency and Implementation"
+ * (queries arranged per KV block, own-block and historical attention
+ * computed separately, merged with an online softmax).
+ *   block_idx  as written by moba_gate_topk (or any caller-made selection in
+ *              the same format: ascending, then -1).  Entries that are
+ *              negative, not below the own block, or not increasing are
+ *              ignored; the own block is always attended.
+ *   out        [total_tokens, num_heads, head_dim], out_dtype (F32 or BF16)
+ *   lse        [total_tokens, num_heads] fp32, natural log
+ *   workspace  device buffer of at least moba_attn_workspace_bytes(...)
+ *              bytes, 256-byte aligned; its contents on entry are ignored
+ * Results are deterministic (no floating-point atomics).
+ */
+moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                          int num_seqs, int total_tokens, int max_seqlen,
+                          int total_blocks, int num_heads, int head_dim,
+                          int block_size, int topk, const int32_t* block_idx,
+                          float softmax_scale, void* out, int out_dtype,
+                          float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes moba_dense_causal_fwd needs (0 when arguments are invalid). */
+size_t moba_dense_workspace_bytes(int dtype, int total_tokens, int total_blocks,
+                                  int num_heads, int head_dim, int block_size);
+
+/*
+ * Dense causal softmax attention (the exact baseline MoBA is compared with:
+ * "MoBA: Learned Block Sparsity for Long-Context Attention", section
+ * "Starting Point: Exact Softmax Attention and Its Cost").
+ *   out[t, h, :] and lse[t, h] as in moba_attn_fwd with J = every token of
+ *   t's sequence up to and including t.
+ * The block geometry (block_size, cu_blocks, total_blocks) only lays out the
+ * transposed-V staging copy in the workspace; any multiple of 64 works.
+ */
+moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, int dtype,
+                                  const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                  int num_seqs, int total_tokens, int max_seqlen,
+                                  int total_blocks, int num_heads, int head_dim,
+                                  int block_size, float softmax_scale, void* out,
+                                  int out_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H_ */

@@ -231,31 +231,52 @@ def moba_reference(Q, K, V, cu_seqlens, block_size, topk, scale, rows=None):
     return dict(rows=rows, out=out, lse=lse, idx=idx, gap=gap, near_tie=near)
 
 
+def select_rows(S, c, topk):
+    """Step 3 for many queries that share their own block c: S [R, c] past
+    scores.  Same rule as ``select_row`` (a stable descending sort keeps the
+    lower block index first among equal scores), vectorised over rows.
+    Returns (idx [R, topk], gap [R], near_tie [R])."""
+    R = S.shape[0]
+    idx = np.full((R, topk), -1, dtype=np.int64)
+    take = min(topk - 1, c)
+    order = np.argsort(-S, axis=1, kind="stable")
+    if take > 0:
+        idx[:, :take] = np.sort(order[:, :take], axis=1)
+    idx[:, take] = c
+    gap = np.full(R, np.inf)
+    near = np.zeros(R, dtype=bool)
+    if topk >= 2 and c >= topk:
+        rr = np.arange(R)
+        a = S[rr, order[:, topk - 2]]
+        b = S[rr, order[:, topk - 1]]
+        gap = a - b
+        near = gap < NEAR_TIE_REL * np.maximum(np.abs(a), np.abs(b))
+    return idx, gap, near
+
+
 def gate_reference(Q, K, cu_seqlens, block_size, topk, rows=None):
-    """Steps 1-3 only (block selection), vectorised per sequence and head:
-    one fp64 matrix product of the queries with the pooled keys, then the
-    per-row causal top-k of ``select_row``."""
+    """Steps 1-3 only (block selection), vectorised: per sequence and head one
+    fp64 product of the queries with the pooled keys, then ``select_rows``
+    for each group of queries sharing an own block."""
     T, H, d = Q.shape
     rows = _rows_by_head(rows, T, H)
     R = len(rows)
     idx = np.full((R, topk), -1, dtype=np.int64)
     gap = np.full(R, np.inf)
     near = np.zeros(R, dtype=bool)
-    order = np.lexsort((rows[:, 0], rows[:, 1]))
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     seq_of = np.searchsorted(cu, rows[:, 0], side="right") - 1
-    groups = {}
-    for r in order:
-        groups.setdefault((int(seq_of[r]), int(rows[r, 1])), []).append(r)
-    for (s, h), rs in groups.items():
+    for s in np.unique(seq_of):
         a, L = int(cu[s]), int(cu[s + 1] - cu[s])
-        kbar = pool_keys_head(K[a:a + L, h, :], L, block_size)
-        rs = np.asarray(rs)
-        tl = rows[rs, 0] - a
-        S = np.asarray(Q[rows[rs, 0], h, :], dtype=np.float64) @ kbar.T
-        for j, r in enumerate(rs):
-            c = int(tl[j]) // block_size
-            idx[r], gap[r], near[r] = select_row(S[j, :c], c, topk)
+        for h in np.unique(rows[seq_of == s, 1]):
+            sel = np.nonzero((seq_of == s) & (rows[:, 1] == h))[0]
+            kbar = pool_keys_head(K[a:a + L, h, :], L, block_size)
+            tl = rows[sel, 0] - a
+            cs = tl // block_size
+            for c in np.unique(cs):
+                g = sel[cs == c]
+                S = np.asarray(Q[rows[g, 0], h, :], dtype=np.float64) @ kbar[:c].T
+                idx[g], gap[g], near[g] = select_rows(S, int(c), topk)
     return dict(rows=rows, idx=idx, gap=gap, near_tie=near)
 
 

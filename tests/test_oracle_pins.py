@@ -237,6 +237,20 @@ def test_gate_reference_agrees_with_rowwise_driver():
     assert np.array_equal(a["near_tie"], b["near_tie"])
 
 
+def test_vectorised_selection_matches_rowwise_with_ties():
+    rng = np.random.default_rng(19)
+    for trial in range(60):
+        c = int(rng.integers(0, 12))
+        topk = int(rng.integers(1, 8))
+        S = rng.integers(-2, 3, size=(9, c)).astype(np.float64)
+        S[::3] += rng.standard_normal((3, c)) * 1e-7   # near-ties as well
+        idx, gap, near = mo.select_rows(S, c, topk)
+        for r in range(9):
+            i1, g1, n1 = mo.select_row(S[r], c, topk)
+            assert idx[r].tolist() == i1.tolist()
+            assert near[r] == n1 and (gap[r] == g1 or (np.isinf(gap[r]) and np.isinf(g1)))
+
+
 def test_near_tie_threshold():
     idx, gap, near = mo.select_row(np.array([1.0, 1.0 + 5e-6, 3.0]), 3, 3)
     assert near and idx.tolist() == [1, 2, 3]
