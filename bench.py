@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""MoBA causal prefill forward on one MI355X: ms per layer, effective TFLOP/s,
+speedup over the library's own dense causal kernel, roofline of the dominant
+kernel and the CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m]
+
+One step is one layer of the MoBA forward over all heads: key pooling, gate
+and top-k, query bucketing, historical-block and own-block attention, merge
+(every call goes through libmoba.so's C ABI).  Inputs, outputs and the
+workspace are resident in HBM before timing starts.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoBA prefill ms/layer + effective TFLOP/s at 32K–1M; speedup vs own dense"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def attended_pairs(seqlens, B, k, H):
+    """(total, historical, own) attended (query, key) pairs of the MoBA forward:
+    per query (t mod B) + 1 own-block keys and B keys per selected past block,
+    min(k - 1, c) of them."""
+    import numpy as np
+    tot = hist = own = 0
+    for L in seqlens:
+        t = np.arange(L, dtype=np.int64)
+        c = t // B
+        o = (t % B + 1).sum()
+        hh = (B * np.minimum(k - 1, c)).sum()
+        own += int(o)
+        hist += int(hh)
+    return H * (own + hist), H * hist, H * own
+
+
+def dense_pairs(seqlens, H):
+    return H * sum(L * (L + 1) // 2 for L in seqlens)
+
+
+def kernel_source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_long_03_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kernel_file):
+    """HBM bytes per launch of the dominant kernel from a committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_hist_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(kernel_file, "common.h"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, rows_target, seconds):
+    """The fp64 oracle on a bounded sample of query rows of head 0."""
+    import numpy as np
+    from oracle import moba_oracle as mo
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    h = 0
+    q = x["q"][:, h:h + 1, :].float().cpu().numpy()
+    k = x["k"][:, h:h + 1, :].float().cpu().numpy()
+    v = x["v"][:, h:h + 1, :].float().cpu().numpy()
+    rng = np.random.default_rng(2000 + w.index)
+    T = w.total_tokens
+    ts = np.sort(rng.choice(T, size=min(rows_target, T), replace=False))
+    rows = np.stack([ts, np.zeros_like(ts)], axis=1)
+    cu = x["cu_seqlens"]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        # pooled keys of the sampled head first (once per head in a full run)
+        t0 = time.perf_counter()
+        mo.moba_reference(q, k, v, cu, w.block_size, w.topk, w.scale, rows=rows[:1])
+        t_first = time.perf_counter() - t0
+        done = 0
+        t0 = time.perf_counter()
+        res = None
+        for i in range(1, len(rows), 8):
+            res = mo.moba_reference(q, k, v, cu, w.block_size, w.topk, w.scale,
+                                    rows=rows[i:i + 8])
+            done += len(rows[i:i + 8])
+            if time.perf_counter() - t0 > seconds:
+                break
+        elapsed = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    sampled = rows[1:1 + done]
+    pairs = 0
+    cu_np = np.asarray(cu)
+    for t in sampled[:, 0]:
+        s = int(np.searchsorted(cu_np, t, side="right") - 1)
+        tl = int(t - cu_np[s])
+        c = tl // w.block_size
+        pairs += (tl % w.block_size) + 1 + w.block_size * min(w.topk - 1, c)
+    flops = 4.0 * w.head_dim * pairs
+    per_row_s = elapsed / max(done, 1)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} seeded query rows of head 0 of the {w.name} workload "
+                   f"(after the head's {T}-token key pooling, {t_first:.1f} s, done once); "
+                   f"fp64 NumPy, BLAS pinned to 1 thread"),
+        "seconds": elapsed,
+        "per_row_ms": per_row_s * 1e3,
+        "extrapolated_layer_s": per_row_s * T * w.heads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="1m")
+    ap.add_argument("--dense-reps", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; MoBA shards by head "
+                          "and the multi-GPU path is not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_03_amd import inputs, moba
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} d{w.head_dim} B{w.block_size} "
+          f"k{w.topk}", file=sys.stderr, flush=True)
+    x = inputs.make_inputs(w, device=dev)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    H, d = w.heads, w.head_dim
+    dt = moba.MOBA_BF16 if w.dtype == "bf16" else moba.MOBA_F32
+    kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((geom.total_tokens, H, w.topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(moba.moba_attn_workspace_bytes(dt, geom.total_tokens, geom.total_blocks,
+                                                    H, d, w.block_size, w.topk),
+                     dtype=torch.uint8, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+
+    def step():
+        moba.moba_pool_keys(k, geom, kbar=kbar)
+        moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+        moba.moba_attn_fwd(q, k, v, geom, w.topk, idx, w.scale, out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    prof = moba.Profiler().attach()
+    prof.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern = prof.summary()
+    prof.reset()
+    print(f"[bench] moba {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # the library's own dense causal kernel on the same inputs
+    del ws
+    dense_ms = None
+    rec_dense_stages = {}
+    if args.dense_reps > 0:
+        dws = torch.empty(moba.moba_dense_workspace_bytes(dt, geom.total_tokens,
+                                                          geom.total_blocks, H, d, w.block_size),
+                          dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(q)
+        dlse = torch.empty_like(lse)
+        moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        prof.reset()
+        t0 = time.perf_counter()
+        for _ in range(args.dense_reps):
+            moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_reps
+        rec_dense_stages = prof.summary()
+        del dout, dws
+        print(f"[bench] dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
+    prof.detach()
+    prof.close()
+
+    pairs, hist_p, own_p = attended_pairs(w.seqlens, w.block_size, w.topk, H)
+    flops = 4.0 * d * pairs
+    eff_tflops = flops / (ms_step * 1e-3) / 1e12
+    stages = {name: {"launches_per_step": n / args.steps, "ms_per_step": ms / args.steps}
+              for name, (n, ms) in kern.items()}
+
+    n_h, ms_h = kern.get("attn_hist", (0, 0.0))
+    avg_h = ms_h / max(n_h, 1)
+    hist_flops = 4.0 * d * hist_p
+    achieved = hist_flops / (avg_h * 1e-3) / 1e12 if avg_h > 0 else 0.0
+    traffic = traffic_from_profiles(w.name, "attn_mfma.hip")
+    roofline = {"kernel": "attn_hist (attn_mfma_kernel, historical blocks)", "bound": "mfma",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "avg_launch_ms": avg_h, "flops_per_launch": hist_flops}
+    n_o, ms_o = kern.get("attn_own", (0, 0.0))
+    own_tflops = 4.0 * d * own_p / (ms_o / max(n_o, 1) * 1e-3) / 1e12 if ms_o > 0 else None
+    n_p, ms_p = kern.get("pool_keys", (0, 0.0))
+    pool_bytes = geom.total_tokens * H * d * q.element_size() + geom.total_blocks * H * d * 4
+    pool_gbps = pool_bytes / (ms_p / max(n_p, 1) * 1e-3) / 1e9 if ms_p > 0 else None
+
+    rec = {
+        "metric": METRIC,
+        "value": eff_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V generated on the GPU)",
+        "config": {"workload": w.name, "seqlens": list(w.seqlens), "heads": H, "head_dim": d,
+                   "block_size": w.block_size, "topk": w.topk,
+                   "sparsity_last_query": 1 - w.topk * w.block_size / max(w.seqlens)},
+        "ms_per_layer": ms_step,
+        "attended_pairs": pairs,
+        "dense_ms": dense_ms,
+        "dense_tflops": (4.0 * d * dense_pairs(w.seqlens, H) / (dense_ms * 1e-3) / 1e12
+                         if dense_ms else None),
+        "speedup_vs_dense": (dense_ms / ms_step) if dense_ms else None,
+        "stages": stages,
+        "dense_stages": {n: {"launches": c, "ms": t} for n, (c, t) in rec_dense_stages.items()},
+        "own_block_tflops": own_tflops,
+        "pool_gbps": pool_gbps,
+        "pool_hbm_frac": pool_gbps / PEAK_HBM_GBPS if pool_gbps else None,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_rows, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,13 +4,51 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
 
 #include "../../include/moba.h"
 #include "launch.h"
 
+struct moba_profiler {
+  struct Rec {
+    std::string name;
+    hipEvent_t start, stop;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> spare;
+};
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local moba_profiler* g_profiler = nullptr;
+
+hipEvent_t profiler_event(moba_profiler* p) {
+  if (!p->spare.empty()) {
+    hipEvent_t e = p->spare.back();
+    p->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one launch group; with a profiler attached, brackets it with events.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  moba_profiler* p = g_profiler;
+  if (!p) return launch();
+  hipEvent_t a = profiler_event(p), b = profiler_event(p);
+  if (!a || !b) return launch();
+  (void)hipEventRecord(a, s);
+  hipError_t e = launch();
+  (void)hipEventRecord(b, s);
+  p->recs.push_back({name, a, b});
+  return e;
+}
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -144,7 +182,9 @@ moba_status moba_pool_keys(const void* k, int dtype, const int32_t* cu_seqlens,
   if (!k || !kbar) return MOBA_ERR_INVALID_ARG;
   moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
                          total_blocks, num_heads, head_dim, block_size);
-  hipError_t e = moba::launch_pool_keys(k, dtype == MOBA_BF16, g, kbar, (hipStream_t)stream);
+  hipError_t e = timed("pool_keys", (hipStream_t)stream, [&] {
+    return moba::launch_pool_keys(k, dtype == MOBA_BF16, g, kbar, (hipStream_t)stream);
+  });
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
@@ -162,8 +202,10 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
   if (!q || !kbar || !block_idx) return MOBA_ERR_INVALID_ARG;
   moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
                          total_blocks, num_heads, head_dim, block_size);
-  hipError_t e = moba::launch_gate_topk(q, dtype == MOBA_BF16, kbar, g, topk, block_idx,
-                                        (hipStream_t)stream);
+  hipError_t e = timed("gate_topk", (hipStream_t)stream, [&] {
+    return moba::launch_gate_topk(q, dtype == MOBA_BF16, kbar, g, topk, block_idx,
+                                  (hipStream_t)stream);
+  });
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
@@ -217,33 +259,48 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
 
   if (bf16) {
     uint16_t* vt = (uint16_t*)(ws + L.vt);
-    if ((e = moba::launch_v_transpose(v, g, vt, s)) != hipSuccess) return hip_fail(e);
-    if ((e = moba::launch_bucket(block_idx, g, topk, moba::kMfmaTileQ, counts, offsets,
-                                 tile_offsets, list, s)) != hipSuccess)
-      return hip_fail(e);
-    if ((e = moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list, offsets,
-                                         tile_offsets, tiles, (uint16_t*)o_part, lse_part,
-                                         s)) != hipSuccess)
-      return hip_fail(e);
-    if ((e = moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale, (uint16_t*)o_part,
-                                        lse_part, s)) != hipSuccess)
-      return hip_fail(e);
-  } else {
-    if ((e = moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
-                                 tile_offsets, list, s)) != hipSuccess)
-      return hip_fail(e);
-    if ((e = moba::launch_attn_f32_hist((const float*)q, (const float*)k, (const float*)v, g,
-                                        topk, softmax_scale, list, offsets,
-                                        hist_entries_bound(g, topk), (float*)o_part, lse_part,
-                                        s)) != hipSuccess)
-      return hip_fail(e);
-    if ((e = moba::launch_attn_f32_own((const float*)q, (const float*)k, (const float*)v, g,
-                                       topk, softmax_scale, (float*)o_part, lse_part, s)) !=
+    if ((e = timed("v_transpose", s, [&] { return moba::launch_v_transpose(v, g, vt, s); })) !=
         hipSuccess)
       return hip_fail(e);
+    if ((e = timed("bucket", s, [&] {
+           return moba::launch_bucket(block_idx, g, topk, moba::kMfmaTileQ, counts, offsets,
+                                      tile_offsets, list, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_hist", s, [&] {
+           return moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list, offsets,
+                                              tile_offsets, tiles, (uint16_t*)o_part, lse_part,
+                                              s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_own", s, [&] {
+           return moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale,
+                                             (uint16_t*)o_part, lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+  } else {
+    if ((e = timed("bucket", s, [&] {
+           return moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
+                                      tile_offsets, list, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_hist", s, [&] {
+           return moba::launch_attn_f32_hist((const float*)q, (const float*)k, (const float*)v,
+                                             g, topk, softmax_scale, list, offsets,
+                                             hist_entries_bound(g, topk), (float*)o_part,
+                                             lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_own", s, [&] {
+           return moba::launch_attn_f32_own((const float*)q, (const float*)k, (const float*)v,
+                                            g, topk, softmax_scale, (float*)o_part, lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
   }
-  if ((e = moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, out, out_bf16, lse,
-                              s)) != hipSuccess)
+  if ((e = timed("merge", s, [&] {
+         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, out, out_bf16,
+                                   lse, s);
+       })) != hipSuccess)
     return hip_fail(e);
   return MOBA_OK;
 }
@@ -285,17 +342,89 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
   hipError_t e;
   if (bf16) {
     uint16_t* vt = (uint16_t*)workspace;
-    if ((e = moba::launch_v_transpose(v, g, vt, s)) != hipSuccess) return hip_fail(e);
-    if ((e = moba::launch_attn_mfma_dense(q, k, vt, g, softmax_scale, out,
-                                          out_dtype == MOBA_BF16, lse, s)) != hipSuccess)
+    if ((e = timed("v_transpose", s, [&] { return moba::launch_v_transpose(v, g, vt, s); })) !=
+        hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_dense", s, [&] {
+           return moba::launch_attn_mfma_dense(q, k, vt, g, softmax_scale, out,
+                                               out_dtype == MOBA_BF16, lse, s);
+         })) != hipSuccess)
       return hip_fail(e);
   } else {
-    if ((e = moba::launch_attn_f32_dense((const float*)q, (const float*)k, (const float*)v, g,
-                                         softmax_scale, out, out_dtype == MOBA_BF16, lse, s)) !=
-        hipSuccess)
+    if ((e = timed("attn_dense", s, [&] {
+           return moba::launch_attn_f32_dense((const float*)q, (const float*)k,
+                                              (const float*)v, g, softmax_scale, out,
+                                              out_dtype == MOBA_BF16, lse, s);
+         })) != hipSuccess)
       return hip_fail(e);
   }
   return MOBA_OK;
+}
+
+moba_status moba_profiler_create(moba_profiler** out) {
+  if (!out) return MOBA_ERR_INVALID_ARG;
+  *out = new moba_profiler();
+  return MOBA_OK;
+}
+
+moba_status moba_profiler_attach(moba_profiler* p) {
+  g_profiler = p;
+  return MOBA_OK;
+}
+
+moba_status moba_profiler_reset(moba_profiler* p) {
+  if (!p) return MOBA_ERR_INVALID_ARG;
+  for (auto& r : p->recs) {
+    p->spare.push_back(r.start);
+    p->spare.push_back(r.stop);
+  }
+  p->recs.clear();
+  return MOBA_OK;
+}
+
+moba_status moba_profiler_read(moba_profiler* p, const char* name, int* launches,
+                               double* total_ms) {
+  if (!p || !name || !launches || !total_ms) return MOBA_ERR_INVALID_ARG;
+  int n = 0;
+  double ms = 0.0;
+  for (auto& r : p->recs) {
+    if (r.name != name) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e);
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e);
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return MOBA_OK;
+}
+
+moba_status moba_profiler_names(moba_profiler* p, char* buf, size_t len) {
+  if (!p || !buf || len == 0) return MOBA_ERR_INVALID_ARG;
+  std::string all;
+  std::vector<std::string> seen;
+  for (auto& r : p->recs) {
+    bool dup = false;
+    for (auto& x : seen) dup = dup || x == r.name;
+    if (dup) continue;
+    seen.push_back(r.name);
+    if (!all.empty()) all += ",";
+    all += r.name;
+  }
+  std::strncpy(buf, all.c_str(), len - 1);
+  buf[len - 1] = '\0';
+  return MOBA_OK;
+}
+
+void moba_profiler_destroy(moba_profiler* p) {
+  if (!p) return;
+  if (g_profiler == p) g_profiler = nullptr;
+  moba_profiler_reset(p);
+  for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  delete p;
 }
 
 }  // extern "C"

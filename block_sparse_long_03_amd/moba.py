@@ -29,7 +29,9 @@ MOBA_BF16 = 1
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_attn_workspace_bytes", "moba_attn_fwd",
-           "moba_dense_workspace_bytes", "moba_dense_causal_fwd"]
+           "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
+           "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
+           "moba_profiler_names", "moba_profiler_destroy"]
 
 _lib = None
 
@@ -72,6 +74,19 @@ def lib():
     L.moba_dense_workspace_bytes.argtypes = [i32] * 6
     L.moba_dense_causal_fwd.restype = i32
     L.moba_dense_causal_fwd.argtypes = [vp, vp, vp, i32] + geo + [f32, vp, i32, vp, vp, sz, vp]
+    L.moba_profiler_create.restype = i32
+    L.moba_profiler_create.argtypes = [ctypes.POINTER(vp)]
+    L.moba_profiler_attach.restype = i32
+    L.moba_profiler_attach.argtypes = [vp]
+    L.moba_profiler_reset.restype = i32
+    L.moba_profiler_reset.argtypes = [vp]
+    L.moba_profiler_read.restype = i32
+    L.moba_profiler_read.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(i32),
+                                     ctypes.POINTER(ctypes.c_double)]
+    L.moba_profiler_names.restype = i32
+    L.moba_profiler_names.argtypes = [vp, ctypes.c_char_p, sz]
+    L.moba_profiler_destroy.restype = None
+    L.moba_profiler_destroy.argtypes = [vp]
     _lib = L
     return L
 
@@ -211,6 +226,45 @@ def moba_dense_causal_fwd(q, k, v, geom, scale, out=None, out_dtype=None, lse=No
         _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return out, lse
+
+
+class Profiler:
+    """Per-kernel HIP-event timing of the library's launches on this thread."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("moba_profiler_create", lib().moba_profiler_create(ctypes.byref(h)))
+        self.handle = h
+
+    def attach(self):
+        _check("moba_profiler_attach", lib().moba_profiler_attach(self.handle))
+        return self
+
+    def detach(self):
+        _check("moba_profiler_attach", lib().moba_profiler_attach(None))
+
+    def reset(self):
+        _check("moba_profiler_reset", lib().moba_profiler_reset(self.handle))
+
+    def read(self, name):
+        n = ctypes.c_int()
+        ms = ctypes.c_double()
+        _check("moba_profiler_read", lib().moba_profiler_read(
+            self.handle, name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+        return n.value, ms.value
+
+    def names(self):
+        buf = ctypes.create_string_buffer(4096)
+        _check("moba_profiler_names", lib().moba_profiler_names(self.handle, buf, 4096))
+        return [x for x in buf.value.decode().split(",") if x]
+
+    def summary(self):
+        return {nm: self.read(nm) for nm in self.names()}
+
+    def close(self):
+        if self.handle:
+            lib().moba_profiler_destroy(self.handle)
+            self.handle = None
 
 
 def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):

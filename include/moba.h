@@ -179,6 +179,33 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
                                   int out_dtype, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement support (not part of the computation).
+ * A profiler attached to the calling thread brackets every kernel launch the
+ * library makes from that thread with a pair of HIP events on the launch's
+ * stream and accumulates, per kernel name, the number of launches and their
+ * total duration.  The profiler owns its events (host-side HIP objects; no
+ * device memory); the results of the computation do not depend on it.
+ *   moba_profiler_create   returns a new profiler in *out
+ *   moba_profiler_attach   attaches p to the calling thread (NULL detaches)
+ *   moba_profiler_reset    forgets all recorded launches
+ *   moba_profiler_read     waits for the recorded events and returns the
+ *                          launches and total milliseconds of kernel `name`
+ *                          (0 and 0.0 if it never ran); names are the
+ *                          kernels' short names, e.g. "attn_hist"
+ *   moba_profiler_names    writes the distinct kernel names seen so far as a
+ *                          comma-separated list into buf (truncated to len)
+ *   moba_profiler_destroy  frees p (detach it first)
+ */
+typedef struct moba_profiler moba_profiler;
+moba_status moba_profiler_create(moba_profiler** out);
+moba_status moba_profiler_attach(moba_profiler* p);
+moba_status moba_profiler_reset(moba_profiler* p);
+moba_status moba_profiler_read(moba_profiler* p, const char* name, int* launches,
+                               double* total_ms);
+moba_status moba_profiler_names(moba_profiler* p, char* buf, size_t len);
+void moba_profiler_destroy(moba_profiler* p);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
@@ -109,6 +109,15 @@ def test_workspace_sizes(L):
     assert b > a > 0 and f > 0
     # the o partials dominate: T * H * k * d elements
     assert a >= 1000 * 2 * 3 * 128 * 2
+
+
+def test_profiler_without_launches(L):
+    p = moba.Profiler()
+    p.attach()
+    assert p.read("attn_hist") == (0, 0.0)
+    assert p.names() == []
+    p.detach()
+    p.close()
 
 
 def test_empty_batch_is_a_no_op(L):
