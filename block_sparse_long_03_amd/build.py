@@ -32,28 +32,31 @@ CFLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
+def _compile(src, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = ([HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
+           + [f"-D{d}" for d in defines])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=True, out=LIB, defines=()):
+    """Compiles every source (optionally with extra -D defines) and links `out`."""
+    build_dir = BUILD if out == LIB else os.path.join(BUILD, os.path.basename(out) + ".d")
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -118,14 +118,18 @@ long long hist_entries_bound(const moba::Geo& g, int topk) {
 }
 
 long long hist_tiles_bound(const moba::Geo& g, int topk) {
-  if (topk < 2) return 0;
-  const long long e = hist_entries_bound(g, topk);
-  return (e + moba::kMfmaTileQ - 1) / moba::kMfmaTileQ + (long long)g.num_heads * g.total_blocks;
+  return moba::hist_tiles_bound(g.total_tokens, g.total_blocks, g.num_heads, topk);
 }
 
 }  // namespace
 
 namespace moba {
+
+long long hist_tiles_bound(long long T, long long NB, long long H, long long topk) {
+  if (topk < 2) return 0;
+  const long long e = T * H * (topk - 1);
+  return (e + kMfmaTileQ - 1) / kMfmaTileQ + H * NB;
+}
 
 AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long long H,
                                     long long D, long long B, long long topk) {
@@ -144,12 +148,15 @@ AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long l
   w.lse_part = take((size_t)(T * H * topk) * 4);
   w.o_part = take((size_t)(T * H * topk * D) * (bf16 ? 2 : 4));
   w.vt = take(bf16 ? (size_t)(NB * B * H * D) * 2 : 0);
+  w.tile_info = take(bf16 ? (size_t)hist_tiles_bound(T, NB, H, topk) * 16 : 0);
+  w.vmax = take((size_t)H * 4);
   w.total = off;
   return w;
 }
 
 size_t dense_workspace_bytes(bool bf16, long long NB, long long H, long long D, long long B) {
-  return align_up(bf16 ? (size_t)(NB * B * H * D) * 2 : 0) + kAlign;
+  if (!bf16) return kAlign;  // the fp32 path stages nothing
+  return align_up((size_t)(NB * B * H * D) * 2) + align_up((size_t)H * 4) + kAlign;
 }
 
 }  // namespace moba
@@ -253,24 +260,25 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
   int32_t* list = (int32_t*)(ws + L.list);
   float* lse_part = (float*)(ws + L.lse_part);
   void* o_part = ws + L.o_part;
+  uint32_t* vmax = (uint32_t*)(ws + L.vmax);
   hipStream_t s = (hipStream_t)stream;
   const bool out_bf16 = out_dtype == MOBA_BF16;
   hipError_t e;
 
   if (bf16) {
     uint16_t* vt = (uint16_t*)(ws + L.vt);
-    if ((e = timed("v_transpose", s, [&] { return moba::launch_v_transpose(v, g, vt, s); })) !=
+    int4* tile_info = (int4*)(ws + L.tile_info);
+    if ((e = timed("v_stage", s, [&] { return moba::launch_v_transpose(v, g, vmax, vt, s); })) !=
         hipSuccess)
       return hip_fail(e);
     if ((e = timed("bucket", s, [&] {
            return moba::launch_bucket(block_idx, g, topk, moba::kMfmaTileQ, counts, offsets,
-                                      tile_offsets, list, s);
+                                      tile_offsets, list, tile_info, tiles, s);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_hist", s, [&] {
-           return moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list, offsets,
-                                              tile_offsets, tiles, (uint16_t*)o_part, lse_part,
-                                              s);
+           return moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list,
+                                              tile_info, tiles, (uint16_t*)o_part, lse_part, s);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_own", s, [&] {
@@ -281,7 +289,7 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
   } else {
     if ((e = timed("bucket", s, [&] {
            return moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
-                                      tile_offsets, list, s);
+                                      tile_offsets, list, nullptr, 0, s);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_hist", s, [&] {
@@ -298,8 +306,8 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
       return hip_fail(e);
   }
   if ((e = timed("merge", s, [&] {
-         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, out, out_bf16,
-                                   lse, s);
+         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, vmax, out,
+                                   out_bf16, lse, s);
        })) != hipSuccess)
     return hip_fail(e);
   return MOBA_OK;
@@ -342,11 +350,12 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
   hipError_t e;
   if (bf16) {
     uint16_t* vt = (uint16_t*)workspace;
-    if ((e = timed("v_transpose", s, [&] { return moba::launch_v_transpose(v, g, vt, s); })) !=
+    uint32_t* vmax = (uint32_t*)((char*)workspace + need - align_up((size_t)num_heads * 4));
+    if ((e = timed("v_stage", s, [&] { return moba::launch_v_transpose(v, g, vmax, vt, s); })) !=
         hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_dense", s, [&] {
-           return moba::launch_attn_mfma_dense(q, k, vt, g, softmax_scale, out,
+           return moba::launch_attn_mfma_dense(q, k, vt, vmax, g, softmax_scale, out,
                                                out_dtype == MOBA_BF16, lse, s);
          })) != hipSuccess)
       return hip_fail(e);

@@ -1,6 +1,6 @@
 // bf16 MFMA block attention for gfx950 (CDNA4), fp32 accumulation.
 //
-// One tile = up to 128 query rows (4 waves x 32) against a contiguous key
+// One tile = up to 128 or 256 query rows (4 waves x 32 or 64) against a contiguous key
 // range of one sequence and head:
 //   historical: the gathered queries that selected KV block j, all B keys of
 //               block j, no mask ("MoBA: Learned Block Sparsity for
@@ -15,8 +15,9 @@
 // (A = 32 keys x 16 dims from LDS, B = the wave's 32 queries from registers),
 // so every lane owns one query column and 16 of the 32 keys; the softmax
 // statistics need one cross-lane exchange (lane ^ 32).  The probabilities are
-// rounded to bf16 in place and used directly as the B operand of
-// O^T += V^T P^T; V^T comes from a staging copy whose key order inside each
+// rounded to fp16 in place and used directly as the B operand of
+// O^T += V^T P^T (fp16 MFMA: probabilities carry 11 significant bits); V^T
+// comes from an fp16 staging copy (exact for bf16 V, scaled per head) whose key order inside each
 // group of 16 matches the MFMA output rows, so both operands are single
 // 16-byte LDS reads.  K and V^T chunks of 64 keys are double-buffered in LDS
 // and prefetched through registers while the previous chunk is computed.
@@ -27,10 +28,24 @@ namespace moba {
 
 enum { kModeHist = 0, kModeOwn = 1, kModeDense = 2 };
 
+// max / sum of a value and the same register of lane (lane ^ 32): one
+// v_permlane32_swap, which hands each half the other half's value
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct MfmaArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const uint16_t* vt;
+  const uint16_t* vt;          // fp16 V^T staging copy, scaled per head by 2^-e
+  const uint32_t* vmax_bits;   // per-head max |v| (fp32 bits): dense mode scales back
   const int32_t* cu_seqlens;
   const int32_t* cu_blocks;
   int num_seqs, total_tokens, H, block_size, topk, NB;
@@ -38,18 +53,22 @@ struct MfmaArgs {
   int units_per_seq;   // own: max blocks per sequence
   float scale2;        // softmax scale * log2(e)
   const int32_t* list;
-  const int32_t* offsets;
-  const int32_t* tile_offsets;
-  void* o_out;  // hist/own: bf16 partials [T, H, topk, D]; dense: out [T, H, D]
+  const int4* tile_info;  // hist: {key, first entry, end entry, 0} per tile, key < 0 past the end
+  void* o_out;  // hist/own: fp16 partials [T, H, topk, D] (V units); dense: out [T, H, D]
   float* lse_out;
 };
 
 constexpr int kTK = 64;     // keys per LDS chunk
 constexpr int kWaves = 4;
+constexpr int kQT = kMfmaTileQ / (kWaves * 32);  // 32-query column tiles per wave
+// Lazy rescaling: the running max used as the exponent base only moves when a
+// new score exceeds it by more than 2^8, so the O accumulators are rescaled
+// rarely; probabilities stay below 256 (exact in the final normalisation).
+constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
-  constexpr int TQ = kWaves * 32;
+template <int D, int MODE, bool OUT_BF16, int QT>
+__global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArgs a) {
+  constexpr int TQ = kWaves * 32 * QT;
   constexpr int KS = D / 16;   // MFMA k-steps of the QK^T product
   constexpr int DT = D / 32;   // 32-row tiles of O^T
   constexpr int KROW = D + 8;  // LDS row strides in bf16 elements (16 B pad)
@@ -67,13 +86,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
 
   // ---------------- tile decode ----------------
   int h, seq_start, seq_len, key_lo, key_hi, gb_base;
-  int qtok = -1, qpos = 0x7fffffff;
-  long long oidx = 0;
+  int qtok[QT], qpos[QT];
+  long long oidx[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) { qtok[qt] = -1; qpos[qt] = 0x7fffffff; oidx[qt] = 0; }
   if (MODE == kModeHist) {
-    const int nkeys = a.H * a.NB;
-    const int tile = blockIdx.x;
-    if (tile >= a.tile_offsets[nkeys]) return;
-    const int key = upper_index(a.tile_offsets, nkeys, tile);
+    const int4 ti = a.tile_info[blockIdx.x];
+    const int key = ti.x;
+    if (key < 0) return;
     h = key / a.NB;
     const int gb = key - h * a.NB;
     const int s = seq_of_block(a.cu_blocks, a.num_seqs, gb);
@@ -81,13 +101,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
     gb_base = a.cu_blocks[s];
     key_lo = (gb - gb_base) * a.block_size;
     key_hi = min(key_lo + a.block_size, seq_len);
-    const int e0 = a.offsets[key] + (tile - a.tile_offsets[key]) * TQ;
-    const int e1 = min(a.offsets[key + 1], e0 + TQ);
-    const int j = e0 + w * 32 + l32;
-    if (j < e1) {
-      const int ent = a.list[j];
-      qtok = ent / a.topk;
-      oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int j = ti.y + (w * QT + qt) * 32 + l32;
+      if (j < ti.z) {
+        const int ent = a.list[j];
+        qtok[qt] = ent / a.topk;
+        oidx[qt] = ((long long)qtok[qt] * a.H + h) * a.topk + (ent - qtok[qt] * a.topk);
+      }
     }
   } else {
     h = blockIdx.y;
@@ -111,62 +132,91 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
     }
     if (q_lo >= q_hi) return;
     key_hi = q_hi;
-    const int p = q_lo + w * 32 + l32;
-    if (p < q_hi) {
-      qtok = seq_start + p;
-      qpos = p;
-      oidx = (MODE == kModeOwn) ? ((long long)qtok * a.H + h) * a.topk + (a.topk - 1)
-                                : (long long)qtok * a.H + h;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int p = q_lo + (w * QT + qt) * 32 + l32;
+      if (p < q_hi) {
+        qtok[qt] = seq_start + p;
+        qpos[qt] = p;
+        oidx[qt] = (MODE == kModeOwn) ? ((long long)qtok[qt] * a.H + h) * a.topk + (a.topk - 1)
+                                      : (long long)qtok[qt] * a.H + h;
+      }
     }
   }
-  const bool qvalid = qtok >= 0;
   // wave-level query extent (for chunk skipping and masking)
-  const uint64_t any_valid = __ballot(qvalid);
-  int wq_min = qvalid ? qpos : 0x7fffffff;
-  int wq_max = qvalid ? qpos : -1;
+  bool any_q = false;
+  int wq_min = 0x7fffffff, wq_max = -1;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    if (qtok[qt] >= 0) {
+      any_q = true;
+      wq_min = min(wq_min, qpos[qt]);
+      wq_max = max(wq_max, qpos[qt]);
+    }
+  }
+  const uint64_t any_valid = __ballot(any_q);
   for (int o = 32; o >= 1; o >>= 1) {
     wq_min = min(wq_min, __shfl_xor(wq_min, o));
     wq_max = max(wq_max, __shfl_xor(wq_max, o));
   }
 
   // ---------------- Q fragments (B operand) ----------------
-  bf16x8 qreg[KS];
-  {
-    const uint16_t* qp = a.q + ((size_t)(qvalid ? qtok : 0) * a.H + h) * D + 8 * hf;
+  bf16x8 qreg[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const bool qv = qtok[qt] >= 0;
+    const uint16_t* qp = a.q + ((size_t)(qv ? qtok[qt] : 0) * a.H + h) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
-      if (qvalid) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      qreg[ks] = __builtin_bit_cast(bf16x8, wv);
+      if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      qreg[qt][ks] = __builtin_bit_cast(bf16x8, wv);
     }
   }
 
   // ---------------- chunk loader ----------------
+  // Every thread moves the same 16-byte segments of each chunk; the per-chunk
+  // base addresses are wave-uniform, the per-thread offsets fixed 32-bit values.
   const int nchunks = (key_hi - key_lo + kTK - 1) / kTK;
+  const size_t krow_bytes = (size_t)a.H * D * 2;
+  const char* kseq = (const char*)a.k + ((size_t)seq_start * a.H + h) * D * 2;
+  uint32_t koff[KSEG], voff[VSEG];
+  int krow[KSEG];
+#pragma unroll
+  for (int i = 0; i < KSEG; ++i) {
+    const int seg = tid + 256 * i;
+    krow[i] = seg / (D / 8);
+    koff[i] = (uint32_t)(krow[i] * krow_bytes + (seg % (D / 8)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VSEG; ++i) {
+    const int seg = tid + 256 * i;
+    voff[i] = (uint32_t)(((seg / (kTK / 8)) * a.block_size + (seg % (kTK / 8)) * 8) * 2);
+  }
   u32x4 kbuf[KSEG], vbuf[VSEG];
   auto load_chunk = [&](int ch) {
     const int kp0 = key_lo + ch * kTK;
+    const char* kb = kseq + (size_t)kp0 * krow_bytes;
+    if (kp0 + kTK <= seq_len) {
 #pragma unroll
-    for (int i = 0; i < KSEG; ++i) {
-      const int seg = tid + 256 * i;
-      const int r = seg / (D / 8), c = seg % (D / 8);
-      const int kp = kp0 + r;
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (kp < seq_len)
-        wv = *reinterpret_cast<const u32x4*>(a.k + ((size_t)(seq_start + kp) * a.H + h) * D + c * 8);
-      kbuf[i] = wv;
+      for (int i = 0; i < KSEG; ++i) kbuf[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KSEG; ++i) {
+        u32x4 wv = {0u, 0u, 0u, 0u};
+        if (kp0 + krow[i] < seq_len) wv = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+        kbuf[i] = wv;
+      }
     }
     const int gb = gb_base + kp0 / a.block_size;
     const int off = kp0 % a.block_size;
-    const bool gb_ok = gb < a.NB;
-    const uint16_t* vb = a.vt + ((size_t)(gb_ok ? gb : 0) * a.H + h) * D * (size_t)a.block_size + off;
+    if (gb < a.NB) {
+      const char* vb = (const char*)(a.vt + ((size_t)gb * a.H + h) * D * (size_t)a.block_size + off);
 #pragma unroll
-    for (int i = 0; i < VSEG; ++i) {
-      const int seg = tid + 256 * i;
-      const int r = seg / (kTK / 8), c = seg % (kTK / 8);
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (gb_ok) wv = *reinterpret_cast<const u32x4*>(vb + (size_t)r * a.block_size + c * 8);
-      vbuf[i] = wv;
+      for (int i = 0; i < VSEG; ++i) vbuf[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VSEG; ++i) vbuf[i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store_chunk = [&](int buf) {
@@ -185,12 +235,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
   };
 
   // ---------------- main loop ----------------
-  f32x16 O[DT];
+  f32x16 O[QT][DT];
+  float m_use[QT], l_run[QT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    m_use[qt] = -INFINITY;
+    l_run[qt] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[qt][dt][r] = 0.f;
+  }
   const float scale2 = a.scale2;
 
   load_chunk(0);
@@ -205,54 +260,66 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
       const bool need_mask = MODE != kModeHist && kp0 + kTK - 1 > wq_min;
 #pragma unroll
       for (int sc = 0; sc < 2; ++sc) {
-        f32x16 S;
+        f32x16 S[QT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = 0.f;
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[qt][r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * sc + l32) * KROW + 16 * ks + 8 * hf]);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], S, 0, 0, 0);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qt][ks], S[qt], 0, 0, 0);
         }
-        // S[r] is the score of query (lane & 31) with key
+        // S[qt][r] is the score of query column (lane & 31) of tile qt with key
         //   kp0 + 32 sc + 8 (r / 4) + 4 hf + (r % 4)
-        if (need_mask) {
+        f16x8 P[QT][2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kpos = kp0 + 32 * sc + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (kpos > qpos) S[r] = -INFINITY;
+        for (int qt = 0; qt < QT; ++qt) {
+          if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kpos = kp0 + 32 * sc + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (kpos > qpos[qt]) S[qt][r] = -INFINITY;
+            }
           }
+          float mx = S[qt][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qt][r]);
+          mx = max_with_partner(mx);
+          const float cand = mx * scale2;
+          if (__ballot(cand > m_use[qt] + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_use[qt], cand);
+            const float alpha =
+                m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use[qt] - m_new);
+            m_use[qt] = m_new;
+            l_run[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) O[qt][dt][r] *= alpha;
+          }
+          const float base = m_use[qt] == -INFINITY ? 0.f : m_use[qt];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[qt][r] = __builtin_amdgcn_exp2f(fmaf(S[qt][r], scale2, -base));
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) P[qt][mm][i] = (_Float16)S[qt][8 * mm + i];
+          float ls = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ls += S[qt][r];
+          l_run[qt] += ls;
         }
-        float mx = S[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * scale2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[r], scale2, -m_use));
-          S[r] = p;
-          ls += p;
-        }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-        bf16x8 P[2];
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) P[mm][i] = (__bf16)S[8 * mm + i];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][(32 * dt + l32) * VROW + 32 * sc + 16 * mm + 8 * hf]);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[mm], O[dt], 0, 0, 0);
+            const f16x8 va = *reinterpret_cast<const f16x8*>(&Vs[buf][(32 * dt + l32) * VROW + 32 * sc + 16 * mm + 8 * hf]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+              O[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, P[qt][mm], O[qt][dt], 0, 0, 0);
           }
         }
       }
@@ -262,33 +329,49 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
   }
 
   // ---------------- epilogue ----------------
-  if (!qvalid) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  const float lse_val = (m_run + log2f(l_tot)) * kLn2;
-  // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4) of query (lane & 31)
-  if (MODE == kModeDense && !OUT_BF16) {
-    float* op = (float*)a.o_out + (size_t)oidx * D;
+  float out_scale = 1.f;
+  if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    // both lanes of a query column take the same branch
+    if (qtok[qt] < 0) continue;
+    const float l_tot = sum_with_partner(l_run[qt]);
+    const float inv = out_scale / l_tot;
+    const float lse_val = (m_use[qt] + log2f(l_tot)) * kLn2;
+    // O[qt][dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
+    if (MODE == kModeDense && !OUT_BF16) {
+      float* op = (float*)a.o_out + (size_t)oidx[qt] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv, O[dt][4 * g + 2] * inv,
-                    O[dt][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
-      }
-  } else {
-    uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4 = {O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv,
+                      O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
+        }
+    } else if (MODE == kModeDense) {
+      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx[qt] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 v2 = {pack_bf16x2(O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv),
-                    pack_bf16x2(O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v2 = {pack_bf16x2(O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv),
+                      pack_bf16x2(O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+        }
+    } else {
+      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx[qt] * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v2 = {pack_f16x2(O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv),
+                      pack_f16x2(O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+        }
+    }
+    if (hf == 0) a.lse_out[oidx[qt]] = lse_val;
   }
-  if (hf == 0) a.lse_out[oidx] = lse_val;
 }
 
 static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, const Geo& g,
@@ -311,21 +394,19 @@ static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, cons
 
 hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* vt,
                                  const Geo& g, int topk, float scale, const int32_t* list,
-                                 const int32_t* offsets, const int32_t* tile_offsets,
-                                 long long max_tiles, uint16_t* o_part, float* lse_part,
-                                 hipStream_t st) {
+                                 const int4* tile_info, long long max_tiles, uint16_t* o_part,
+                                 float* lse_part, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, topk, scale);
   a.list = list;
-  a.offsets = offsets;
-  a.tile_offsets = tile_offsets;
+  a.tile_info = tile_info;
   a.o_out = o_part;
   a.lse_out = lse_part;
   dim3 grid((unsigned)max_tiles);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true, kQT>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true, kQT>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -340,24 +421,25 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
   a.lse_out = lse_part;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.num_heads);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true, kQT>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true, kQT>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
-                                  const Geo& g, float scale, void* out, bool out_bf16,
-                                  float* lse, hipStream_t st) {
+                                  const uint32_t* vmax_bits, const Geo& g, float scale,
+                                  void* out, bool out_bf16, float* lse, hipStream_t st) {
   if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, 1, scale);
+  a.vmax_bits = vmax_bits;
   a.tiles_per_unit = (g.max_seqlen + kMfmaTileQ - 1) / kMfmaTileQ;
   a.units_per_seq = 1;
   a.o_out = out;
   a.lse_out = lse;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.num_heads);
 #define MOBA_DENSE(D, OB) \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB>), grid, dim3(256), 0, st, a)
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB, kQT>), grid, dim3(256), 0, st, a)
   if (g.head_dim == 128) { if (out_bf16) MOBA_DENSE(128, true); else MOBA_DENSE(128, false); }
   else { if (out_bf16) MOBA_DENSE(64, true); else MOBA_DENSE(64, false); }
 #undef MOBA_DENSE

@@ -132,13 +132,30 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int32_t* __restrict__
   if (threadIdx.x == 0) { offsets[n] = carry[0]; tile_offsets[n] = carry[1]; }
 }
 
+__global__ __launch_bounds__(256) void tile_info_kernel(const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ tile_offsets,
+                                                        int nkeys, int tile_q, long long max_tiles,
+                                                        int4* __restrict__ info) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= max_tiles) return;
+  const int total = tile_offsets[nkeys];
+  if (t >= total) {
+    info[t] = make_int4(-1, 0, 0, 0);
+    return;
+  }
+  const int key = upper_index(tile_offsets, nkeys, (int)t);
+  const int e0 = offsets[key] + ((int)t - tile_offsets[key]) * tile_q;
+  const int e1 = min(offsets[key + 1], e0 + tile_q);
+  info[t] = make_int4(key, e0, e1, 0);
+}
+
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* list, hipStream_t st) {
+                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st) {
   const int n = g.num_heads * g.total_blocks;
   if (n > 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
@@ -156,23 +173,55 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
     hipLaunchKernelGGL((bucket_pass_kernel<true>), grid, dim3(256), 0, st, block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, g.num_heads,
                        g.total_blocks, g.block_size, topk, counts, offsets, list);
+  if (tile_info && max_tiles > 0)
+    hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
+                       st, offsets, tile_offsets, n, tile_q, max_tiles, tile_info);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// V^T staging: vt[((gb*H + h)*d + e)*B + p] = V[token of key pi(p), h, e]
-// where, inside every group of 16 keys, storage position p holds key
-// pi(p) = 8*((p & 7) >> 2) + 4*(p >> 3) + (p & 3) (quads 1 and 2 swapped).
-// This is the key order in which a lane of the 32x32x16 MFMA holds its eight
-// softmax probabilities, so each lane's eight V^T values are contiguous.
-// Keys past the end of the sequence are stored as zero.
+// V staging for the MFMA kernels, in two passes:
+//  1. vmax_bits[h] = fp32 bits of max |v| over head h (atomicMax on the bit
+//     patterns, which order like the values for non-negative floats);
+//  2. vt[((gb*H + h)*d + e)*B + p] = fp16(V[token of key pi(p), h, e] * 2^-e_h)
+//     with e_h = v_exponent(vmax_bits[h]) (exact for bf16 input), where,
+//     inside every group of 16 keys, storage position p holds key
+//     pi(p) = 8*((p & 7) >> 2) + 4*(p >> 3) + (p & 3) (quads 1 and 2
+//     swapped): the key order in which a lane of the 32x32x16 MFMA holds its
+//     eight softmax probabilities, so each lane's eight V^T values are one
+//     16-byte read.  Keys past the end of the sequence are stored as zero.
 // ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v,
+                                                   int total_tokens, int hd, int head_dim,
+                                                   uint32_t* __restrict__ vmax_bits) {
+  __shared__ uint32_t red[256];
+  const int col0 = blockIdx.y * 64;          // 64 columns of one head
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  const int t0 = blockIdx.x * 2048;
+  uint32_t m = 0u;
+  for (int t = t0 + ty; t < min(total_tokens, t0 + 2048); t += 32) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(v + (size_t)t * hd + col0 + tx * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, (w[i] << 16) & 0x7fffffffu);
+      m = max(m, w[i] & 0x7fff0000u);
+    }
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int st = 128; st >= 1; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + st]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMax(&vmax_bits[col0 / head_dim], red[0]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void v_transpose_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int H,
-    int block_size, uint16_t* __restrict__ vt) {
-  __shared__ uint16_t tile[64][D + 2];
+    int block_size, const uint32_t* __restrict__ vmax_bits, uint16_t* __restrict__ vt) {
+  __shared__ float tile[64][D + 1];
   const int chunks_per_block = block_size / 64;
   const int gb = blockIdx.x / chunks_per_block;
   const int ci = blockIdx.x % chunks_per_block;
@@ -182,6 +231,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
   seq_span(cu_seqlens, s, total_tokens, &start, &len);
   const int local = (gb - cu_blocks[s]) * block_size + ci * 64;
   const int nk = max(0, min(64, len - local));
+  const float scale = __builtin_ldexpf(1.0f, -v_exponent(vmax_bits[h]));
   constexpr int SEG = D / 8;
   for (int i = threadIdx.x; i < 64 * SEG; i += 256) {
     const int r = i / SEG, c = i % SEG;
@@ -189,8 +239,8 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
     if (r < nk) w = *reinterpret_cast<const u32x4*>(v + ((size_t)(start + local + r) * H + h) * D + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tile[r][c * 8 + 2 * e] = (uint16_t)(w[e] & 0xffffu);
-      tile[r][c * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+      tile[r][c * 8 + 2 * e] = lo_bf16(w[e]) * scale;
+      tile[r][c * 8 + 2 * e + 1] = hi_bf16(w[e]) * scale;
     }
   }
   __syncthreads();
@@ -200,7 +250,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
     uint32_t packed[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t two[2];
+      float two[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int p = seg * 8 + 2 * j + u;
@@ -208,68 +258,133 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
         const int key = g16 + 8 * ((pp & 7) >> 2) + 4 * (pp >> 3) + (pp & 3);
         two[u] = tile[key][e];
       }
-      packed[j] = two[0] | (two[1] << 16);
+      packed[j] = pack_f16x2(two[0], two[1]);
     }
     u32x4 outv = {packed[0], packed[1], packed[2], packed[3]};
     *reinterpret_cast<u32x4*>(dst + (size_t)e * block_size + seg * 8) = outv;
   }
 }
 
-hipError_t launch_v_transpose(const void* v, const Geo& g, uint16_t* vt, hipStream_t st) {
+hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, uint16_t* vt,
+                              hipStream_t st) {
   if (g.total_blocks == 0) return hipSuccess;
+  const int hd = g.num_heads * g.head_dim;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, st, (int32_t*)vmax_bits,
+                     g.num_heads);
+  hipLaunchKernelGGL(vmax_kernel, dim3((g.total_tokens + 2047) / 2048, hd / 64), dim3(256), 0, st,
+                     (const uint16_t*)v, g.total_tokens, hd, g.head_dim, vmax_bits);
   dim3 grid(g.total_blocks * (g.block_size / 64), g.num_heads);
   if (g.head_dim == 128)
     hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)v,
                        g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads,
-                       g.block_size, vt);
+                       g.block_size, vmax_bits, vt);
   else
     hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, st, (const uint16_t*)v,
                        g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads,
-                       g.block_size, vt);
+                       g.block_size, vmax_bits, vt);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// merge: one wave per (token, head) row
+// merge: 16 lanes per (token, head) row, 16 rows per workgroup.  Each lane
+// owns D/16 consecutive output dims; the part weights exp(lse_p - lse) go
+// through LDS so that every lane can stream its slice of all the parts with
+// several loads in flight.
 // ---------------------------------------------------------------------------
-template <int D, bool kPartBf16, bool kOutBf16>
+template <int D, bool kPartF16, bool kOutBf16>
 __global__ __launch_bounds__(256) void merge_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     int num_seqs, int total_tokens, int H, int block_size, int topk,
     const void* __restrict__ o_part, const float* __restrict__ lse_part,
-    void* __restrict__ out, float* __restrict__ lse) {
-  const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (long long)total_tokens * H) return;
-  const int t = (int)(row / H);
-  const int s = upper_index(cu_seqlens, num_seqs, t);
-  const int c = (t - cu_seqlens[s]) / block_size;
-  const int32_t* irow = block_idx + row * topk;
-  const int nh = count_hist(irow, topk, c);
-  const int nparts = nh + 1;
-  // part i < nh lives in slot i; the own block in slot topk - 1
-  const int my_slot = lane < nh ? lane : topk - 1;
-  const float my_lse = lane < nparts ? lse_part[row * topk + my_slot] : -INFINITY;
-  const float mx = wave_max(my_lse);
-  const float wsum = wave_sum(lane < nparts ? expf(my_lse - mx) : 0.f);
-  const float tot = mx + logf(wsum);
-  const float my_w = lane < nparts ? expf(my_lse - tot) : 0.f;
-  constexpr int PER = D / 64;  // elements per lane
+    const uint32_t* __restrict__ vmax_bits, void* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PER = D / 16;  // output dims per lane
+  __shared__ float wts[16][64];
+  __shared__ int slots[16][64];
+  const int r16 = threadIdx.x >> 4;  // row within the workgroup
+  const int li = threadIdx.x & 15;   // lane within the row
+  const long long row = (long long)blockIdx.x * 16 + r16;
+  const bool valid = row < (long long)total_tokens * H;
+  int nparts = 0;
+  float tot = 0.f;
+  if (valid) {
+    const int t = (int)(row / H);
+    const int s = upper_index(cu_seqlens, num_seqs, t);
+    const int c = (t - cu_seqlens[s]) / block_size;
+    const int nh = count_hist(block_idx + row * topk, topk, c);
+    nparts = nh + 1;
+    // part i < nh lives in slot i; the own block in slot topk - 1
+    float l4[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = li + 16 * u;
+      const int slot = i < nh ? i : topk - 1;
+      l4[u] = i < nparts ? lse_part[row * topk + slot] : -INFINITY;
+      mx = fmaxf(mx, l4[u]);
+      if (i < 64) slots[r16][i] = slot;
+    }
+    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sum += (li + 16 * u < nparts) ? expf(l4[u] - mx) : 0.f;
+    for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 16);
+    tot = mx + logf(sum);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = li + 16 * u;
+      if (i < 64) wts[r16][i] = i < nparts ? expf(l4[u] - tot) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const float wi = __shfl(my_w, i);
-    const int slot = i < nh ? i : topk - 1;
-    const size_t base = ((size_t)row * topk + slot) * D + lane * PER;
-    if (kPartBf16) {
-      const uint16_t* p = (const uint16_t*)o_part + base;
-      if (PER == 2) {
-        const uint32_t wv = *reinterpret_cast<const uint32_t*>(p);
-        acc[0] = fmaf(wi, lo_bf16(wv), acc[0]);
-        acc[PER - 1] = fmaf(wi, hi_bf16(wv), acc[PER - 1]);
+  const size_t rbase = (size_t)row * topk;
+  int i = 0;
+  for (; i + 4 <= nparts; i += 4) {
+    float v[4][PER];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t base = (rbase + slots[r16][i + u]) * D + li * PER;
+      if (kPartF16) {
+        const uint16_t* p = (const uint16_t*)o_part + base;
+        if (PER == 8) {
+          const u32x4 w4 = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[u][2 * e] = lo_f16(w4[e]); v[u][2 * e + 1] = hi_f16(w4[e]); }
+        } else {
+          const u32x2 w2 = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) { v[u][2 * e] = lo_f16(w2[e]); v[u][2 * e + 1] = hi_f16(w2[e]); }
+        }
       } else {
-        acc[0] = fmaf(wi, bf16_bits_to_f32(p[0]), acc[0]);
+        const float* p = (const float*)o_part + base;
+#pragma unroll
+        for (int e = 0; e < PER; e += 4) {
+          const f32x4 f4 = *reinterpret_cast<const f32x4*>(p + e);
+#pragma unroll
+          for (int z = 0; z < 4; ++z) v[u][e + z] = f4[z];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wi = wts[r16][i + u];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wi, v[u][e], acc[e]);
+    }
+  }
+  for (; i < nparts; ++i) {
+    const size_t base = (rbase + slots[r16][i]) * D + li * PER;
+    const float wi = wts[r16][i];
+    if (kPartF16) {
+      const uint16_t* p = (const uint16_t*)o_part + base;
+#pragma unroll
+      for (int e = 0; e < PER; e += 2) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(p + e);
+        acc[e] = fmaf(wi, lo_f16(w2), acc[e]);
+        acc[e + 1] = fmaf(wi, hi_f16(w2), acc[e + 1]);
       }
     } else {
       const float* p = (const float*)o_part + base;
@@ -277,34 +392,43 @@ __global__ __launch_bounds__(256) void merge_kernel(
       for (int e = 0; e < PER; ++e) acc[e] = fmaf(wi, p[e], acc[e]);
     }
   }
-  const size_t ob = (size_t)row * D + lane * PER;
-  if (kOutBf16) {
-    uint16_t* o = (uint16_t*)out + ob;
+  if (kPartF16) {
+    // fp16 partials are in units of 2^-e_h (the staged V's scale)
+    const float sc = __builtin_ldexpf(1.0f, v_exponent(vmax_bits[row % H]));
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = f32_to_bf16_bits(acc[e]);
+    for (int e = 0; e < PER; ++e) acc[e] *= sc;
+  }
+  const size_t ob = (size_t)row * D + li * PER;
+  if (kOutBf16) {
+    uint32_t* o = (uint32_t*)((uint16_t*)out + ob);
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) o[e / 2] = pack_bf16x2(acc[e], acc[e + 1]);
   } else {
     float* o = (float*)out + ob;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = acc[e];
+    for (int e = 0; e < PER; e += 4) {
+      f32x4 f4 = {acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+      *reinterpret_cast<f32x4*>(o + e) = f4;
+    }
   }
-  if (lane == 0) lse[row] = tot;
+  if (li == 0) lse[row] = tot;
 }
 
 hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
-                        bool part_bf16, const float* lse_part, void* out, bool out_bf16,
-                        float* lse, hipStream_t st) {
+                        bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
+                        void* out, bool out_bf16, float* lse, hipStream_t st) {
   const long long rows = (long long)g.total_tokens * g.num_heads;
   if (rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((rows + 3) / 4));
+  dim3 grid((unsigned)((rows + 15) / 16));
 #define MOBA_MERGE(D, PB, OB)                                                            \
   hipLaunchKernelGGL((merge_kernel<D, PB, OB>), grid, dim3(256), 0, st, block_idx,       \
                      g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.block_size, \
-                     topk, o_part, lse_part, out, lse)
+                     topk, o_part, lse_part, vmax_bits, out, lse)
   if (g.head_dim == 128) {
-    if (part_bf16) { if (out_bf16) MOBA_MERGE(128, true, true); else MOBA_MERGE(128, true, false); }
+    if (part_f16) { if (out_bf16) MOBA_MERGE(128, true, true); else MOBA_MERGE(128, true, false); }
     else { if (out_bf16) MOBA_MERGE(128, false, true); else MOBA_MERGE(128, false, false); }
   } else {
-    if (part_bf16) { if (out_bf16) MOBA_MERGE(64, true, true); else MOBA_MERGE(64, true, false); }
+    if (part_f16) { if (out_bf16) MOBA_MERGE(64, true, true); else MOBA_MERGE(64, true, false); }
     else { if (out_bf16) MOBA_MERGE(64, false, true); else MOBA_MERGE(64, false, false); }
   }
 #undef MOBA_MERGE

@@ -11,6 +11,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -30,6 +31,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// fp16 <-> fp32 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// V is staged in fp16 for the PV products, scaled per head by 2^-e so that
+// the head's largest |v| stays below 2^15.  vmax_bits is the fp32 bit
+// pattern of that largest |v| (bf16 values convert exactly, only the scale
+// moves); e = 0 for any head whose values are below 32768.
+__device__ __forceinline__ int v_exponent(uint32_t vmax_bits) {
+  const int x = (int)((vmax_bits >> 23) & 0xffu) - 126;  // vmax < 2^x
+  return max(0, x - 15);
 }
 
 // Index of the sequence that owns global block `gb` (largest s with

@@ -23,16 +23,22 @@ struct Geo {
 // Query tile (rows per workgroup) of the bf16 MFMA attention kernels and of
 // the fp32 attention kernels; the bucket scan cuts the per-block query lists
 // into tiles of this many rows.
-constexpr int kMfmaTileQ = 128;
+#ifndef MOBA_ATTN_QT
+#define MOBA_ATTN_QT 1  // 32-query column tiles per wave of the MFMA attention kernels
+#endif
+constexpr int kMfmaTileQ = 128 * MOBA_ATTN_QT;
 constexpr int kF32TileQ = 1;
 
 // Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
 struct AttnWorkspace {
-  size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, total;
+  size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, tile_info, vmax, total;
 };
 AttnWorkspace attn_workspace_layout(bool bf16, long long total_tokens, long long total_blocks,
                                     long long num_heads, long long head_dim,
                                     long long block_size, long long topk);
+// Upper bound on the number of historical tiles of kMfmaTileQ rows.
+long long hist_tiles_bound(long long total_tokens, long long total_blocks, long long num_heads,
+                           long long topk);
 size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_heads,
                              long long head_dim, long long block_size);
 
@@ -42,26 +48,30 @@ hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const G
 
 // Query bucketing: counts per (head, KV block), exclusive scans of entries and
 // of tiles, and the scatter of (token, slot) entries into per-block lists.
+// With tile_info, also writes {key, first entry, end entry, 0} for each of
+// the max_tiles tiles of tile_q rows (key -1 past the last tile).
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* list, hipStream_t st);
+                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st);
 
-// Transposed, key-permuted copy of V per (block, head) for the MFMA kernels.
-hipError_t launch_v_transpose(const void* v, const Geo& g, uint16_t* vt, hipStream_t st);
+// Transposed, key-permuted fp16 copy of V per (block, head) for the MFMA
+// kernels, scaled per head by 2^-e (vmax_bits[h] receives max |v|).
+hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, uint16_t* vt,
+                              hipStream_t st);
 
 // bf16 MFMA attention.  mode: 0 historical blocks (gathered queries, partials),
 // 1 own block (causal, partials), 2 dense causal (final output).
+// Partials (hist, own) are fp16 in the staged V's units; dense scales back.
 hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* vt,
                                  const Geo& g, int topk, float scale, const int32_t* list,
-                                 const int32_t* offsets, const int32_t* tile_offsets,
-                                 long long max_tiles, uint16_t* o_part, float* lse_part,
-                                 hipStream_t st);
+                                 const int4* tile_info, long long max_tiles, uint16_t* o_part,
+                                 float* lse_part, hipStream_t st);
 hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt,
                                 const Geo& g, int topk, float scale, uint16_t* o_part,
                                 float* lse_part, hipStream_t st);
 hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
-                                  const Geo& g, float scale, void* out, bool out_bf16,
-                                  float* lse, hipStream_t st);
+                                  const uint32_t* vmax_bits, const Geo& g, float scale,
+                                  void* out, bool out_bf16, float* lse, hipStream_t st);
 
 // fp32 VALU attention (one wave per query row and key range).
 hipError_t launch_attn_f32_hist(const float* q, const float* k, const float* v, const Geo& g,
@@ -77,7 +87,7 @@ hipError_t launch_attn_f32_dense(const float* q, const float* k, const float* v,
 
 // Online-softmax combine of the partials of every (token, head) row.
 hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
-                        bool part_bf16, const float* lse_part, void* out, bool out_bf16,
-                        float* lse, hipStream_t st);
+                        bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
+                        void* out, bool out_bf16, float* lse, hipStream_t st);
 
 }  // namespace moba

@@ -159,6 +159,25 @@ def test_moba_edge_cases(dev, w):
     print(w.name, st)
 
 
+def test_moba_peaky_softmax(dev):
+    """Sharp attention (queries scaled by 4, scores of std ~4): a few keys
+    dominate each softmax, the regime where rounding of the probabilities
+    shows most in the output and the log-sum-exp."""
+    w = inputs.custom([2048, 900], 2, 128, 128, 4, "bf16", name="peaky")
+    _say(w.name)
+    x = inputs.make_inputs(w, device=dev, seed=21)
+    x["q"].mul_(4)  # exact in bf16
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    out, lse, idx = moba.forward(x["q"], x["k"], x["v"], geom, w.topk, w.scale,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.stack(np.meshgrid(np.arange(0, w.total_tokens, 3), np.arange(w.heads),
+                                indexing="ij"), -1).reshape(-1, 2)
+    st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
+                                w.scale, out, lse, idx, rows, parity.BF16_TOL)
+    print("peaky", st)
+
+
 def test_k_ge_n_matches_own_dense_kernel(dev):
     w = inputs.custom([520, 1000], 2, 128, 128, 16, "bf16", name="k>n-vs-dense")
     x, geom, out, lse, idx = _run(w, dev, seed=3, out_dtype=torch.float32)
