@@ -59,7 +59,8 @@ struct MfmaArgs {
 };
 
 constexpr int kTK = 64;     // keys per LDS chunk
-constexpr int kWaves = 4;
+constexpr int kWaves = kMfmaWaves;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kQT = kMfmaTileQ / (kWaves * 32);  // 32-query column tiles per wave
 // Lazy rescaling: the running max used as the exponent base only moves when a
 // new score exceeds it by more than 2^8, so the O accumulators are rescaled
@@ -67,14 +68,16 @@ constexpr int kQT = kMfmaTileQ / (kWaves * 32);  // 32-query column tiles per wa
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D, int MODE, bool OUT_BF16, int QT>
-__global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerSimd)))
+void attn_mfma_kernel(MfmaArgs a) {
   constexpr int TQ = kWaves * 32 * QT;
   constexpr int KS = D / 16;   // MFMA k-steps of the QK^T product
   constexpr int DT = D / 32;   // 32-row tiles of O^T
   constexpr int KROW = D + 8;  // LDS row strides in bf16 elements (16 B pad)
   constexpr int VROW = kTK + 8;
-  constexpr int KSEG = kTK * D / 8 / 256;  // 16-byte segments per thread per chunk
-  constexpr int VSEG = D * kTK / 8 / 256;
+  constexpr int NSEG = kTK * D / 8;  // 16-byte segments of a K (or V^T) chunk
+  constexpr int KSEG = (NSEG + kThreads - 1) / kThreads;  // per thread
+  constexpr int VSEG = KSEG;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VROW];
 
@@ -143,22 +146,12 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArg
       }
     }
   }
-  // wave-level query extent (for chunk skipping and masking)
-  bool any_q = false;
-  int wq_min = 0x7fffffff, wq_max = -1;
+  // smallest query position of the wave: chunks past it need the causal mask
+  int wq_min = 0x7fffffff;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    if (qtok[qt] >= 0) {
-      any_q = true;
-      wq_min = min(wq_min, qpos[qt]);
-      wq_max = max(wq_max, qpos[qt]);
-    }
-  }
-  const uint64_t any_valid = __ballot(any_q);
-  for (int o = 32; o >= 1; o >>= 1) {
-    wq_min = min(wq_min, __shfl_xor(wq_min, o));
-    wq_max = max(wq_max, __shfl_xor(wq_max, o));
-  }
+  for (int qt = 0; qt < QT; ++qt)
+    if (qtok[qt] >= 0) wq_min = min(wq_min, qpos[qt]);
+  for (int o = 32; o >= 1; o >>= 1) wq_min = min(wq_min, __shfl_xor(wq_min, o));
 
   // ---------------- Q fragments (B operand) ----------------
   bf16x8 qreg[QT][KS];
@@ -184,15 +177,18 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArg
   int krow[KSEG];
 #pragma unroll
   for (int i = 0; i < KSEG; ++i) {
-    const int seg = tid + 256 * i;
+    const int seg = min(tid + kThreads * i, NSEG - 1);
     krow[i] = seg / (D / 8);
     koff[i] = (uint32_t)(krow[i] * krow_bytes + (seg % (D / 8)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < VSEG; ++i) {
-    const int seg = tid + 256 * i;
+    const int seg = min(tid + kThreads * i, NSEG - 1);
     voff[i] = (uint32_t)(((seg / (kTK / 8)) * a.block_size + (seg % (kTK / 8)) * 8) * 2);
   }
+  // V^T source of the next chunk to load: block gb_next at offset off_next
+  int gb_next = gb_base + key_lo / a.block_size;
+  int off_next = key_lo % a.block_size;
   u32x4 kbuf[KSEG], vbuf[VSEG];
   auto load_chunk = [&](int ch) {
     const int kp0 = key_lo + ch * kTK;
@@ -208,145 +204,165 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArg
         kbuf[i] = wv;
       }
     }
-    const int gb = gb_base + kp0 / a.block_size;
-    const int off = kp0 % a.block_size;
-    if (gb < a.NB) {
-      const char* vb = (const char*)(a.vt + ((size_t)gb * a.H + h) * D * (size_t)a.block_size + off);
+    if (gb_next < a.NB) {
+      const char* vb =
+          (const char*)(a.vt + ((size_t)gb_next * a.H + h) * D * (size_t)a.block_size + off_next);
 #pragma unroll
       for (int i = 0; i < VSEG; ++i) vbuf[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < VSEG; ++i) vbuf[i] = u32x4{0u, 0u, 0u, 0u};
     }
+    off_next += kTK;
+    if (off_next == a.block_size) { off_next = 0; ++gb_next; }
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KSEG; ++i) {
-      const int seg = tid + 256 * i;
-      const int r = seg / (D / 8), c = seg % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * KROW + c * 8]) = kbuf[i];
+      const int seg = tid + kThreads * i;
+      if (NSEG % kThreads == 0 || seg < NSEG) {
+        const int r = seg / (D / 8), c = seg % (D / 8);
+        *reinterpret_cast<u32x4*>(&Ks[buf][r * KROW + c * 8]) = kbuf[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < VSEG; ++i) {
-      const int seg = tid + 256 * i;
-      const int r = seg / (kTK / 8), c = seg % (kTK / 8);
-      *reinterpret_cast<u32x4*>(&Vs[buf][r * VROW + c * 8]) = vbuf[i];
+      const int seg = tid + kThreads * i;
+      if (NSEG % kThreads == 0 || seg < NSEG) {
+        const int r = seg / (kTK / 8), c = seg % (kTK / 8);
+        *reinterpret_cast<u32x4*>(&Vs[buf][r * VROW + c * 8]) = vbuf[i];
+      }
     }
   };
 
   // ---------------- main loop ----------------
-  f32x16 O[QT][DT];
-  float m_use[QT], l_run[QT];
+  // Software pipeline over 32-key steps: the QK^T product of the next step is
+  // issued while the probabilities of the current step are formed, and the
+  // current PV product runs while the next step's row max is taken, so the
+  // matrix cores and the vector ALUs of a wave work side by side.
+  static_assert(QT == 1, "one 32-query column tile per wave");
+  f32x16 O[DT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_use[qt] = -INFINITY;
-    l_run[qt] = 0.f;
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+  float m_use = -INFINITY, l_run = 0.f;
+  const float scale2 = a.scale2;
+  const int qp = qpos[0];
+
+  auto qk = [&](int buf, int sc) {
+    f32x16 S;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * sc + l32) * KROW + 16 * ks + 8 * hf]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[0][ks], S, 0, 0, 0);
+    }
+    return S;
+  };
+  // S[r] is the score of query column (lane & 31) with key kp + 8 (r / 4) + 4 hf + (r % 4)
+  auto mask = [&](f32x16& S, int kp) {
+    if (MODE != kModeHist && kp + 31 > wq_min) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kp + 8 * (r >> 2) + 4 * hf + (r & 3) > qp) S[r] = -INFINITY;
+    }
+  };
+  auto row_max = [&](const f32x16& S) {
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    return max_with_partner(mx);
+  };
+  auto rescale = [&](float mx) {
+    const float cand = mx * scale2;
+    if (__ballot(cand > m_use + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_use, cand);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
+      m_use = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+  };
+  auto probs = [&](f32x16 S, f16x8* P) {
+    const float base = m_use == -INFINITY ? 0.f : m_use;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale2, -base));
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) P[mm][i] = (_Float16)S[8 * mm + i];
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ls += S[r];
+    l_run += ls;
+  };
+  auto pv = [&](int buf, int sc, const f16x8* P) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) O[qt][dt][r] = 0.f;
-  }
-  const float scale2 = a.scale2;
+      for (int mm = 0; mm < 2; ++mm) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(&Vs[buf][(32 * dt + l32) * VROW + 32 * sc + 16 * mm + 8 * hf]);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, P[mm], O[dt], 0, 0, 0);
+      }
+  };
 
   load_chunk(0);
   store_chunk(0);
+  if (nchunks > 1) load_chunk(1);
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) load_chunk(ch + 1);
-    const int kp0 = key_lo + ch * kTK;
-    const bool active = any_valid != 0 && kp0 <= wq_max;
-    if (active) {
-      const bool need_mask = MODE != kModeHist && kp0 + kTK - 1 > wq_min;
-#pragma unroll
-      for (int sc = 0; sc < 2; ++sc) {
-        f32x16 S[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) S[qt][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * sc + l32) * KROW + 16 * ks + 8 * hf]);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qt][ks], S[qt], 0, 0, 0);
-        }
-        // S[qt][r] is the score of query column (lane & 31) of tile qt with key
-        //   kp0 + 32 sc + 8 (r / 4) + 4 hf + (r % 4)
-        f16x8 P[QT][2];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          if (need_mask) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kpos = kp0 + 32 * sc + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (kpos > qpos[qt]) S[qt][r] = -INFINITY;
-            }
-          }
-          float mx = S[qt][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qt][r]);
-          mx = max_with_partner(mx);
-          const float cand = mx * scale2;
-          if (__ballot(cand > m_use[qt] + kRescaleSlack) != 0) {
-            const float m_new = fmaxf(m_use[qt], cand);
-            const float alpha =
-                m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use[qt] - m_new);
-            m_use[qt] = m_new;
-            l_run[qt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) O[qt][dt][r] *= alpha;
-          }
-          const float base = m_use[qt] == -INFINITY ? 0.f : m_use[qt];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) S[qt][r] = __builtin_amdgcn_exp2f(fmaf(S[qt][r], scale2, -base));
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) P[qt][mm][i] = (_Float16)S[qt][8 * mm + i];
-          float ls = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ls += S[qt][r];
-          l_run[qt] += ls;
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 va = *reinterpret_cast<const f16x8*>(&Vs[buf][(32 * dt + l32) * VROW + 32 * sc + 16 * mm + 8 * hf]);
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-              O[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, P[qt][mm], O[qt][dt], 0, 0, 0);
-          }
-        }
-      }
+  f32x16 Sa = qk(0, 0);
+  mask(Sa, key_lo);
+  rescale(row_max(Sa));
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const int kp0 = key_lo + c * kTK;
+    f16x8 P[2];
+    // first 32 keys of chunk c; the QK^T of its second 32 keys is in flight
+    f32x16 Sb = qk(buf, 1);
+    probs(Sa, P);
+    pv(buf, 0, P);
+    mask(Sb, kp0 + 32);
+    const float mxb = row_max(Sb);
+    if (c + 1 < nchunks) store_chunk(buf ^ 1);
+    __syncthreads();  // chunk c + 1 is in LDS
+    if (c + 2 < nchunks) load_chunk(c + 2);
+    rescale(mxb);
+    // second 32 keys of chunk c; the QK^T of chunk c + 1's first 32 keys is in
+    // flight (on the last chunk it reads a stale buffer and is discarded)
+    Sa = qk(buf ^ 1, 0);
+    probs(Sb, P);
+    pv(buf, 1, P);
+    if (c + 1 < nchunks) {
+      mask(Sa, kp0 + kTK);
+      rescale(row_max(Sa));
     }
-    if (ch + 1 < nchunks) store_chunk(buf ^ 1);
-    __syncthreads();
+    __syncthreads();  // every wave is done with chunk c's buffer
   }
 
   // ---------------- epilogue ----------------
   float out_scale = 1.f;
   if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
+  {
+    constexpr int qt = 0;
     // both lanes of a query column take the same branch
-    if (qtok[qt] < 0) continue;
-    const float l_tot = sum_with_partner(l_run[qt]);
+    if (qtok[qt] < 0) return;
+    const float l_tot = sum_with_partner(l_run);
     const float inv = out_scale / l_tot;
-    const float lse_val = (m_use[qt] + log2f(l_tot)) * kLn2;
-    // O[qt][dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
+    const float lse_val = (m_use + log2f(l_tot)) * kLn2;
+    // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
     if (MODE == kModeDense && !OUT_BF16) {
       float* op = (float*)a.o_out + (size_t)oidx[qt] * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 v4 = {O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv,
-                      O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv};
+          f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv,
+                      O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
         }
     } else if (MODE == kModeDense) {
@@ -355,8 +371,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArg
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          u32x2 v2 = {pack_bf16x2(O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv),
-                      pack_bf16x2(O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv)};
+          u32x2 v2 = {pack_bf16x2(O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv),
+                      pack_bf16x2(O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
         }
     } else {
@@ -365,8 +381,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_mfma_kernel(MfmaArg
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          u32x2 v2 = {pack_f16x2(O[qt][dt][4 * g] * inv, O[qt][dt][4 * g + 1] * inv),
-                      pack_f16x2(O[qt][dt][4 * g + 2] * inv, O[qt][dt][4 * g + 3] * inv)};
+          u32x2 v2 = {pack_f16x2(O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv),
+                      pack_f16x2(O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
         }
     }
@@ -404,9 +420,9 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
   a.lse_out = lse_part;
   dim3 grid((unsigned)max_tiles);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true, kQT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true, kQT>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true, kQT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true, kQT>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -421,9 +437,9 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
   a.lse_out = lse_part;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.num_heads);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true, kQT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true, kQT>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true, kQT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true, kQT>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -439,7 +455,7 @@ hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* 
   a.lse_out = lse;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.num_heads);
 #define MOBA_DENSE(D, OB) \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB, kQT>), grid, dim3(256), 0, st, a)
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB, kQT>), grid, dim3(kThreads), 0, st, a)
   if (g.head_dim == 128) { if (out_bf16) MOBA_DENSE(128, true); else MOBA_DENSE(128, false); }
   else { if (out_bf16) MOBA_DENSE(64, true); else MOBA_DENSE(64, false); }
 #undef MOBA_DENSE

@@ -26,7 +26,15 @@ struct Geo {
 #ifndef MOBA_ATTN_QT
 #define MOBA_ATTN_QT 1  // 32-query column tiles per wave of the MFMA attention kernels
 #endif
-constexpr int kMfmaTileQ = 128 * MOBA_ATTN_QT;
+#ifndef MOBA_ATTN_WAVES
+#define MOBA_ATTN_WAVES 4  // waves per workgroup of the MFMA attention kernels
+#endif
+#ifndef MOBA_ATTN_OCC
+#define MOBA_ATTN_OCC 2  // target waves per SIMD (bounds the kernels' registers)
+#endif
+constexpr int kMfmaWaves = MOBA_ATTN_WAVES;
+constexpr int kMfmaWavesPerSimd = MOBA_ATTN_OCC;
+constexpr int kMfmaTileQ = 32 * MOBA_ATTN_WAVES * MOBA_ATTN_QT;
 constexpr int kF32TileQ = 1;
 
 // Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
