@@ -111,86 +111,125 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-constexpr int kGateRows = 64;     // query tokens per workgroup (one block c)
-constexpr int kGateChunk = 64;    // past blocks scored per pass
+constexpr int kGateRows = 64;    // query tokens per workgroup (they share one own block c)
+constexpr int kGateSpan = 256;   // past blocks per selection pass (4 per lane)
+constexpr int kGateChunk = 64;   // past blocks per scoring step
 constexpr int kGateWaves = 8;
 constexpr int kGateRowsPerWave = kGateRows / kGateWaves;
 
-template <typename T, int D>
-__device__ __forceinline__ void load_q_tile(const T* __restrict__ q, float (*qs)[D + 4],
-                                            int tok0, int nq, int H, int h, int tid);
-
-template <>
-__device__ __forceinline__ void load_q_tile<uint16_t, 128>(const uint16_t* __restrict__ q,
-                                                           float (*qs)[132], int tok0, int nq,
-                                                           int H, int h, int tid) {
-  for (int i = tid; i < kGateRows * 16; i += kGateWaves * 64) {
-    int r = i >> 4, c = i & 15;
-    float v[8];
-    if (r < nq) load8<uint16_t>(q + ((size_t)(tok0 + r) * H + h) * 128 + c * 8, v);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qs[r][c * 8 + e] = v[e];
-  }
-}
-template <>
-__device__ __forceinline__ void load_q_tile<uint16_t, 64>(const uint16_t* __restrict__ q,
-                                                          float (*qs)[68], int tok0, int nq,
-                                                          int H, int h, int tid) {
-  for (int i = tid; i < kGateRows * 8; i += kGateWaves * 64) {
-    int r = i >> 3, c = i & 7;
-    float v[8];
-    if (r < nq) load8<uint16_t>(q + ((size_t)(tok0 + r) * H + h) * 64 + c * 8, v);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qs[r][c * 8 + e] = v[e];
-  }
-}
-template <>
-__device__ __forceinline__ void load_q_tile<float, 128>(const float* __restrict__ q,
-                                                        float (*qs)[132], int tok0, int nq,
-                                                        int H, int h, int tid) {
-  for (int i = tid; i < kGateRows * 32; i += kGateWaves * 64) {
-    int r = i >> 5, c = i & 31;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r < nq) v = *reinterpret_cast<const f32x4*>(q + ((size_t)(tok0 + r) * H + h) * 128 + c * 4);
-    *reinterpret_cast<f32x4*>(&qs[r][c * 4]) = v;
-  }
-}
-template <>
-__device__ __forceinline__ void load_q_tile<float, 64>(const float* __restrict__ q,
-                                                       float (*qs)[68], int tok0, int nq,
-                                                       int H, int h, int tid) {
-  for (int i = tid; i < kGateRows * 16; i += kGateWaves * 64) {
-    int r = i >> 4, c = i & 15;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r < nq) v = *reinterpret_cast<const f32x4*>(q + ((size_t)(tok0 + r) * H + h) * 64 + c * 4);
-    *reinterpret_cast<f32x4*>(&qs[r][c * 4]) = v;
-  }
+// exact split of an fp32 value into three bf16 parts: x = hi + mid + lo
+__device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
+  const float h = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  const float r1 = x - h;
+  const float m = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+  hi = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(h) >> 16));
+  mid = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(m) >> 16));
+  lo = (__bf16)(r1 - m);  // at most 8 significant bits remain: exact
 }
 
-// One workgroup handles 64 consecutive query tokens of one sequence and head.
-// Since B is a multiple of 64 they share their own block c.  Past blocks are
-// scored 64 at a time into LDS (fp32 FMA over d in index order); each wave
-// then keeps, for each of its 8 rows, the running top-(k-1) set in lanes
-// 0..k-2 (ascending block index).  Merging a chunk into the set is an exact
-// radix select over 32-bit order keys (ballot counts), with ties on the
-// threshold key given to the lower block index.
+// Scores of a chunk of up to 64 past blocks for the 64 query rows, written to
+// ss[row][col0 + j].  bf16 queries: s = q . kbar with kbar split exactly into
+// three bf16 parts and the three products summed by v_mfma_f32_32x32x16_bf16
+// (products exact, fp32 accumulation); waves 0..3 each own one 32 x 32 tile.
+template <int D>
+__device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
+                                                 const float* __restrict__ kbar, int H, int h,
+                                                 int gblk0, int nb, int total_blocks,
+                                                 float (*ss)[kGateSpan + 1], int col0, int w,
+                                                 int lane) {
+  if (w >= 4) return;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int bt = w & 1, tt = w >> 1;
+  const int j = 32 * bt + l32;  // block of this lane's A rows
+  const bool ok = j < nb && gblk0 + j < total_blocks;
+  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : 0) * H + h) * D + 8 * hf;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      x0 = *reinterpret_cast<const f32x4*>(kp + 16 * ks);
+      x1 = *reinterpret_cast<const f32x4*>(kp + 16 * ks + 4);
+    }
+    bf16x8 hi, mid, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 a, b, cc;
+      split3(e < 4 ? x0[e] : x1[e - 4], a, b, cc);
+      hi[e] = a;
+      mid[e] = b;
+      lo[e] = cc;
+    }
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qfrag[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qfrag[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qfrag[ks], acc, 0, 0, 0);
+  }
+  // acc[r] = score of block 32 bt + 8 (r / 4) + 4 hf + (r % 4) for token 32 tt + (lane & 31)
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    ss[32 * tt + l32][col0 + 32 * bt + 8 * (r >> 2) + 4 * hf + (r & 3)] = acc[r];
+}
+
+// fp32 queries: plain fp32 FMA over d in index order (LDS tiles of q and kbar)
+template <int D>
+__device__ __forceinline__ void gate_scores_valu(const float (*qs)[D + 4], float (*ks)[D + 4],
+                                                 const float* __restrict__ kbar, int H, int h,
+                                                 int gblk0, int nb, int total_blocks,
+                                                 float (*ss)[kGateSpan + 1], int col0, int tid) {
+  for (int i = tid; i < kGateChunk * (D / 4); i += kGateWaves * 64) {
+    const int j = i / (D / 4), e4 = i % (D / 4);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (j < nb && gblk0 + j < total_blocks)
+      v = *reinterpret_cast<const f32x4*>(kbar + ((size_t)(gblk0 + j) * H + h) * D + e4 * 4);
+    *reinterpret_cast<f32x4*>(&ks[j][e4 * 4]) = v;
+  }
+  __syncthreads();
+  const int ty = tid >> 4;  // rows 2ty, 2ty+1
+  const int tx = tid & 15;  // blocks tx + 16 jj
+  float acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+#pragma unroll 4
+  for (int e = 0; e < D; e += 4) {
+    const f32x4 qa = *reinterpret_cast<const f32x4*>(&qs[2 * ty][e]);
+    const f32x4 qb = *reinterpret_cast<const f32x4*>(&qs[2 * ty + 1][e]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[tx + 16 * jj][e]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[0][jj] = fmaf(qa[u], kv[u], acc[0][jj]);
+        acc[1][jj] = fmaf(qb[u], kv[u], acc[1][jj]);
+      }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    ss[2 * ty][col0 + tx + 16 * jj] = acc[0][jj];
+    ss[2 * ty + 1][col0 + tx + 16 * jj] = acc[1][jj];
+  }
+  __syncthreads();  // ks is reused by the next chunk
+}
+
+// One workgroup handles 64 consecutive query tokens of one sequence and head
+// (B is a multiple of 64, so they share their own block c).  The past blocks
+// are scored into LDS up to 256 at a time; then each wave merges, for each of
+// its 8 rows, those candidates into the running top-(k-1) set held in lanes
+// 0..k-2 (ascending block index).  The merge is an exact radix select over
+// 32-bit order keys with ballot counts; among keys equal to the threshold the
+// lower block indices win.
 template <typename T, int D>
 __global__ __launch_bounds__(512) void gate_topk_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
     int total_tokens, int total_blocks, int tiles_per_seq, int H, int block_size, int topk,
     int32_t* __restrict__ block_idx) {
-  __shared__ __attribute__((aligned(16))) float qs[kGateRows][D + 4];
-  __shared__ __attribute__((aligned(16))) float ks[kGateChunk][D + 4];
-  __shared__ float ss[kGateRows][kGateChunk + 1];
+  constexpr bool kMfma = sizeof(T) == 2;
+  __shared__ float ss[kGateRows][kGateSpan + 1];
   __shared__ uint32_t skey[kGateWaves][64];
   __shared__ int32_t sidx[kGateWaves][64];
 
@@ -216,94 +255,107 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
   for (int i = 0; i < kGateRowsPerWave; ++i) { tkey[i] = 0u; tidx[i] = -1; tcnt[i] = 0; }
 
   if (k1 > 0 && c > 0) {
-    load_q_tile<T, D>(q, qs, start + p0, nq, H, h, tid);
-    const int ty = tid >> 4;   // rows 2ty, 2ty+1
-    const int tx = tid & 15;   // blocks tx + 16 jj
-    for (int base = 0; base < c; base += kGateChunk) {
-      const int nb = min(kGateChunk, c - base);
-      for (int i = tid; i < kGateChunk * (D / 4); i += kGateWaves * 64) {
-        int j = i / (D / 4), e4 = i % (D / 4);
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (j < nb && gb0 + base + j < total_blocks)
-          v = *reinterpret_cast<const f32x4*>(kbar + ((size_t)(gb0 + base + j) * H + h) * D + e4 * 4);
-        *reinterpret_cast<f32x4*>(&ks[j][e4 * 4]) = v;
+    // query operands: bf16 MFMA fragments in registers, or an fp32 LDS tile
+    bf16x8 qfrag[D / 16];
+    if constexpr (kMfma) {
+      const int tok = p0 + 32 * (w >> 1) + (lane & 31);
+      const bool qv = w < 4 && tok < len;
+      const uint16_t* qp = (const uint16_t*)q + ((size_t)(start + (qv ? tok : p0)) * H + h) * D +
+                           8 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 wv = {0u, 0u, 0u, 0u};
+        if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+        qfrag[ks] = __builtin_bit_cast(bf16x8, wv);
       }
-      __syncthreads();
-      float acc[2][4];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-#pragma unroll 4
-      for (int e = 0; e < D; e += 4) {
-        f32x4 qa = *reinterpret_cast<const f32x4*>(&qs[2 * ty][e]);
-        f32x4 qb = *reinterpret_cast<const f32x4*>(&qs[2 * ty + 1][e]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[tx + 16 * jj][e]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[0][jj] = fmaf(qa[u], kv[u], acc[0][jj]);
-            acc[1][jj] = fmaf(qb[u], kv[u], acc[1][jj]);
+    }
+    for (int base = 0; base < c; base += kGateSpan) {
+      const int nspan = min(kGateSpan, c - base);
+      if constexpr (kMfma) {
+        for (int cb = 0; cb < nspan; cb += kGateChunk)
+          gate_scores_mfma<D>(qfrag, kbar, H, h, gb0 + base + cb, min(kGateChunk, nspan - cb),
+                              total_blocks, ss, cb, w, lane);
+        __syncthreads();
+      } else {
+        __shared__ __attribute__((aligned(16))) float qs[kGateRows][D + 4];
+        __shared__ __attribute__((aligned(16))) float ks[kGateChunk][D + 4];
+        if (base == 0) {
+          for (int i = tid; i < kGateRows * (D / 4); i += kGateWaves * 64) {
+            const int r = i / (D / 4), e4 = i % (D / 4);
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (r < nq)
+              v = *reinterpret_cast<const f32x4*>((const float*)q + ((size_t)(start + p0 + r) * H + h) * D + e4 * 4);
+            *reinterpret_cast<f32x4*>(&qs[r][e4 * 4]) = v;
           }
         }
+        for (int cb = 0; cb < nspan; cb += kGateChunk)
+          gate_scores_valu<D>(qs, ks, kbar, H, h, gb0 + base + cb, min(kGateChunk, nspan - cb),
+                              total_blocks, ss, cb, tid);
       }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        ss[2 * ty][tx + 16 * jj] = acc[0][jj];
-        ss[2 * ty + 1][tx + 16 * jj] = acc[1][jj];
-      }
-      __syncthreads();
 
+      // The wave's 8 rows go through the radix select in lockstep (independent
+      // dependency chains).  Order keys of finite scores are >= 1, so key 0
+      // marks "no candidate" (lanes past the span, rows past the tile end,
+      // unused slots of the kept set) and never reaches a threshold >= 1.
+      constexpr int R = kGateRowsPerWave;
+      uint32_t nkey[R][4];
 #pragma unroll
-      for (int i = 0; i < kGateRowsPerWave; ++i) {
-        const int r = w * kGateRowsPerWave + i;
-        if (r >= nq) continue;  // wave-uniform
-        const bool nv = lane < nb;
-        const uint32_t nkey = nv ? order_key(ss[r][lane]) : 0u;
-        const int32_t nidx = base + lane;
-        const bool ov = lane < tcnt[i];
-        const uint32_t okey = tkey[i];
-        const int32_t oidx = tidx[i];
-        const int total = tcnt[i] + nb;
-        if (total <= k1) {
-          if (ov) { skey[w][lane] = okey; sidx[w][lane] = oidx; }
-          if (nv) { skey[w][tcnt[i] + lane] = nkey; sidx[w][tcnt[i] + lane] = nidx; }
-          __builtin_amdgcn_wave_barrier();
-          tkey[i] = skey[w][lane];
-          tidx[i] = sidx[w][lane];
-          tcnt[i] = total;
-        } else {
-          uint32_t prefix = 0u;
-          for (int b = 31; b >= 0; --b) {
-            const uint32_t cand = prefix | (1u << b);
-            const uint64_t mo = __ballot(ov && okey >= cand);
-            const uint64_t mn = __ballot(nv && nkey >= cand);
-            if (__popcll(mo) + __popcll(mn) >= k1) prefix = cand;
-          }
-          const uint32_t thr = prefix;
-          const uint64_t go = __ballot(ov && okey > thr);
-          const uint64_t gn = __ballot(nv && nkey > thr);
-          const int need = k1 - __popcll(go) - __popcll(gn);
-          const uint64_t eo = __ballot(ov && okey == thr);
-          const uint64_t en = __ballot(nv && nkey == thr);
-          const int need_n = need - min(need, (int)__popcll(eo));
-          const bool selo = ov && (okey > thr || (okey == thr && lanes_below(eo) < need));
-          const bool seln = nv && (nkey > thr || (nkey == thr && lanes_below(en) < need_n));
-          const uint64_t so = __ballot(selo);
-          const uint64_t sn = __ballot(seln);
-          __builtin_amdgcn_wave_barrier();
-          if (selo) { skey[w][lanes_below(so)] = okey; sidx[w][lanes_below(so)] = oidx; }
-          if (seln) {
-            const int pos = (int)__popcll(so) + lanes_below(sn);
-            skey[w][pos] = nkey;
-            sidx[w][pos] = nidx;
-          }
-          __builtin_amdgcn_wave_barrier();
-          tkey[i] = skey[w][lane];
-          tidx[i] = sidx[w][lane];
-          tcnt[i] = k1;
+      for (int i = 0; i < R; ++i) {
+        const int r = w * R + i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          nkey[i][j] = (r < nq && lane + 64 * j < nspan) ? order_key(ss[r][lane + 64 * j]) : 0u;
+      }
+      uint32_t prefix[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) prefix[i] = 0u;
+      for (int b = 31; b >= 0; --b) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const uint32_t cand = prefix[i] | (1u << b);
+          int cnt = (int)__popcll(__ballot(tkey[i] >= cand));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cnt += (int)__popcll(__ballot(nkey[i][j] >= cand));
+          if (cnt >= k1) prefix[i] = cand;
         }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        // thr = 0 when there are at most k1 candidates: all of them are kept
+        const uint32_t thr = prefix[i];
+        int need = k1 - (int)__popcll(__ballot(tkey[i] > thr));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) need -= (int)__popcll(__ballot(nkey[i][j] > thr));
+        // keys equal to the threshold: lowest block index first (old set, then new)
+        const uint64_t eo = __ballot(thr != 0u && tkey[i] == thr);
+        const bool so = tkey[i] > thr || (thr != 0u && tkey[i] == thr && lanes_below(eo) < need);
+        need -= min(need, (int)__popcll(eo));
+        bool sn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint64_t en = __ballot(thr != 0u && nkey[i][j] == thr);
+          sn[j] = nkey[i][j] > thr || (thr != 0u && nkey[i][j] == thr && lanes_below(en) < need);
+          need -= min(need, (int)__popcll(en));
+        }
+        // compact: kept old entries, then new ones in block order
+        const uint64_t mo = __ballot(so);
+        int pos0 = (int)__popcll(mo);
+        __builtin_amdgcn_wave_barrier();
+        if (so) { skey[w][lanes_below(mo)] = tkey[i]; sidx[w][lanes_below(mo)] = tidx[i]; }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint64_t mn = __ballot(sn[j]);
+          if (sn[j]) {
+            const int pos = pos0 + lanes_below(mn);
+            skey[w][pos] = nkey[i][j];
+            sidx[w][pos] = base + lane + 64 * j;
+          }
+          pos0 += (int)__popcll(mn);
+        }
+        __builtin_amdgcn_wave_barrier();
+        tkey[i] = lane < pos0 ? skey[w][lane] : 0u;
+        tidx[i] = lane < pos0 ? sidx[w][lane] : -1;
+        tcnt[i] = pos0;
         __builtin_amdgcn_wave_barrier();
       }
       __syncthreads();
