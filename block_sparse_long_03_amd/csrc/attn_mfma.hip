@@ -17,10 +17,17 @@
 // statistics need one cross-lane exchange (lane ^ 32).  The probabilities are
 // rounded to fp16 in place and used directly as the B operand of
 // O^T += V^T P^T (fp16 MFMA: probabilities carry 11 significant bits); V^T
-// comes from an fp16 staging copy (exact for bf16 V, scaled per head) whose key order inside each
-// group of 16 matches the MFMA output rows, so both operands are single
-// 16-byte LDS reads.  K and V^T chunks of 64 keys are double-buffered in LDS
-// and prefetched through registers while the previous chunk is computed.
+// comes from an fp16 staging copy (exact for bf16 V, scaled per head) whose
+// key order inside each group of 16 matches the MFMA output rows, so both
+// operands are single 16-byte LDS reads.
+//
+// K and V^T chunks of 64 keys are double-buffered in LDS and filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4: each wave instruction writes
+// 1 KiB of consecutive LDS, no registers involved) while the previous chunk
+// is computed; one barrier per chunk.  The LDS tiles are unpadded and
+// XOR-swizzled in 16-byte segments so that the MFMA operand reads are free of
+// bank conflicts: rows of 256 B use segment ^ (row & 15), rows of 128 B use
+// segment ^ ((row >> 1) & 7).
 #include "common.h"
 #include "launch.h"
 
@@ -61,25 +68,42 @@ struct MfmaArgs {
 constexpr int kTK = 64;     // keys per LDS chunk
 constexpr int kWaves = kMfmaWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQT = kMfmaTileQ / (kWaves * 32);  // 32-query column tiles per wave
+static_assert(kMfmaTileQ == kWaves * 32, "one 32-query column tile per wave");
+
+// segment swizzle of an LDS tile row (row_bytes 256 or 128)
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row) {
+  return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane i's data lands
+// at dst + 16 i (dst is wave-uniform)
+__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
 // Lazy rescaling: the running max used as the exponent base only moves when a
 // new score exceeds it by more than 2^8, so the O accumulators are rescaled
 // rarely; probabilities stay below 256 (exact in the final normalisation).
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int MODE, bool OUT_BF16, int QT>
+template <int D, int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerSimd)))
 void attn_mfma_kernel(MfmaArgs a) {
-  constexpr int TQ = kWaves * 32 * QT;
-  constexpr int KS = D / 16;   // MFMA k-steps of the QK^T product
-  constexpr int DT = D / 32;   // 32-row tiles of O^T
-  constexpr int KROW = D + 8;  // LDS row strides in bf16 elements (16 B pad)
-  constexpr int VROW = kTK + 8;
-  constexpr int NSEG = kTK * D / 8;  // 16-byte segments of a K (or V^T) chunk
-  constexpr int KSEG = (NSEG + kThreads - 1) / kThreads;  // per thread
-  constexpr int VSEG = KSEG;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VROW];
+  constexpr int TQ = kWaves * 32;
+  constexpr int KS = D / 16;             // MFMA k-steps of the QK^T product
+  constexpr int DT = D / 32;             // 32-row tiles of O^T
+  constexpr int KRB = D * 2;             // bytes of a K row in LDS (256 / 128)
+  constexpr int VRB = kTK * 2;           // bytes of a V^T row in LDS (128)
+  constexpr int KBYTES = kTK * KRB;      // one K chunk
+  constexpr int VBYTES = D * VRB;        // one V^T chunk
+  constexpr int BUF = KBYTES + VBYTES;
+  constexpr int NKI = KBYTES / 1024;     // 1-KiB wave loads per K chunk
+  constexpr int NVI = VBYTES / 1024;
+  constexpr int KIW = (NKI + kWaves - 1) / kWaves;  // per wave
+  constexpr int VIW = (NVI + kWaves - 1) / kWaves;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -89,10 +113,8 @@ void attn_mfma_kernel(MfmaArgs a) {
 
   // ---------------- tile decode ----------------
   int h, seq_start, seq_len, key_lo, key_hi, gb_base;
-  int qtok[QT], qpos[QT];
-  long long oidx[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) { qtok[qt] = -1; qpos[qt] = 0x7fffffff; oidx[qt] = 0; }
+  int qtok = -1, qpos = 0x7fffffff;
+  long long oidx = 0;
   if (MODE == kModeHist) {
     const int4 ti = a.tile_info[blockIdx.x];
     const int key = ti.x;
@@ -104,14 +126,11 @@ void attn_mfma_kernel(MfmaArgs a) {
     gb_base = a.cu_blocks[s];
     key_lo = (gb - gb_base) * a.block_size;
     key_hi = min(key_lo + a.block_size, seq_len);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int j = ti.y + (w * QT + qt) * 32 + l32;
-      if (j < ti.z) {
-        const int ent = a.list[j];
-        qtok[qt] = ent / a.topk;
-        oidx[qt] = ((long long)qtok[qt] * a.H + h) * a.topk + (ent - qtok[qt] * a.topk);
-      }
+    const int j = ti.y + w * 32 + l32;
+    if (j < ti.z) {
+      const int ent = a.list[j];
+      qtok = ent / a.topk;
+      oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
     }
   } else {
     h = blockIdx.y;
@@ -135,112 +154,96 @@ void attn_mfma_kernel(MfmaArgs a) {
     }
     if (q_lo >= q_hi) return;
     key_hi = q_hi;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int p = q_lo + (w * QT + qt) * 32 + l32;
-      if (p < q_hi) {
-        qtok[qt] = seq_start + p;
-        qpos[qt] = p;
-        oidx[qt] = (MODE == kModeOwn) ? ((long long)qtok[qt] * a.H + h) * a.topk + (a.topk - 1)
-                                      : (long long)qtok[qt] * a.H + h;
-      }
+    const int p = q_lo + w * 32 + l32;
+    if (p < q_hi) {
+      qtok = seq_start + p;
+      qpos = p;
+      oidx = (MODE == kModeOwn) ? ((long long)qtok * a.H + h) * a.topk + (a.topk - 1)
+                                : (long long)qtok * a.H + h;
     }
   }
   // smallest query position of the wave: chunks past it need the causal mask
-  int wq_min = 0x7fffffff;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-    if (qtok[qt] >= 0) wq_min = min(wq_min, qpos[qt]);
+  int wq_min = qtok >= 0 ? qpos : 0x7fffffff;
   for (int o = 32; o >= 1; o >>= 1) wq_min = min(wq_min, __shfl_xor(wq_min, o));
 
   // ---------------- Q fragments (B operand) ----------------
-  bf16x8 qreg[QT][KS];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const bool qv = qtok[qt] >= 0;
-    const uint16_t* qp = a.q + ((size_t)(qv ? qtok[qt] : 0) * a.H + h) * D + 8 * hf;
+  bf16x8 qreg[KS];
+  {
+    const bool qv = qtok >= 0;
+    const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.H + h) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
       if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      qreg[qt][ks] = __builtin_bit_cast(bf16x8, wv);
+      qreg[ks] = __builtin_bit_cast(bf16x8, wv);
     }
   }
 
-  // ---------------- chunk loader ----------------
-  // Every thread moves the same 16-byte segments of each chunk; the per-chunk
-  // base addresses are wave-uniform, the per-thread offsets fixed 32-bit values.
+  // ---------------- chunk loads (global -> LDS) ----------------
   const int nchunks = (key_hi - key_lo + kTK - 1) / kTK;
   const size_t krow_bytes = (size_t)a.H * D * 2;
   const char* kseq = (const char*)a.k + ((size_t)seq_start * a.H + h) * D * 2;
-  uint32_t koff[KSEG], voff[VSEG];
-  int krow[KSEG];
+  int krow[KIW];
+  uint32_t koff[KIW], voff[VIW];
 #pragma unroll
-  for (int i = 0; i < KSEG; ++i) {
-    const int seg = min(tid + kThreads * i, NSEG - 1);
-    krow[i] = seg / (D / 8);
-    koff[i] = (uint32_t)(krow[i] * krow_bytes + (seg % (D / 8)) * 16);
+  for (int i = 0; i < KIW; ++i) {
+    const int L = (w + kWaves * i) * 1024 + lane * 16;  // LDS byte this lane fills
+    const int r = L / KRB;
+    const int lseg = ((L % KRB) >> 4) ^ swz<KRB>(r);
+    krow[i] = r;
+    koff[i] = (uint32_t)(r * krow_bytes + lseg * 16);
   }
 #pragma unroll
-  for (int i = 0; i < VSEG; ++i) {
-    const int seg = min(tid + kThreads * i, NSEG - 1);
-    voff[i] = (uint32_t)(((seg / (kTK / 8)) * a.block_size + (seg % (kTK / 8)) * 8) * 2);
+  for (int i = 0; i < VIW; ++i) {
+    const int L = (w + kWaves * i) * 1024 + lane * 16;
+    const int r = L / VRB;
+    const int lseg = ((L % VRB) >> 4) ^ swz<VRB>(r);
+    voff[i] = (uint32_t)(r * a.block_size * 2 + lseg * 16);
   }
-  // V^T source of the next chunk to load: block gb_next at offset off_next
-  int gb_next = gb_base + key_lo / a.block_size;
+  int gb_next = gb_base + key_lo / a.block_size;  // V^T source of the next chunk
   int off_next = key_lo % a.block_size;
-  u32x4 kbuf[KSEG], vbuf[VSEG];
-  auto load_chunk = [&](int ch) {
+  auto load_chunk = [&](int ch, int buf) {
     const int kp0 = key_lo + ch * kTK;
+    char* kl = smem + buf * BUF;
     const char* kb = kseq + (size_t)kp0 * krow_bytes;
-    if (kp0 + kTK <= seq_len) {
+    const bool full = kp0 + kTK <= seq_len;
 #pragma unroll
-      for (int i = 0; i < KSEG; ++i) kbuf[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < KSEG; ++i) {
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        if (kp0 + krow[i] < seq_len) wv = *reinterpret_cast<const u32x4*>(kb + koff[i]);
-        kbuf[i] = wv;
+    for (int i = 0; i < KIW; ++i) {
+      const int j = w + kWaves * i;
+      if (NKI % kWaves == 0 || j < NKI) {
+        // rows past the sequence end repeat its last key (always masked)
+        const char* src = full ? kb + koff[i]
+                               : kb + koff[i] - (size_t)max(0, kp0 + krow[i] - (seq_len - 1)) * krow_bytes;
+        lds_dma16(src, kl + j * 1024);
       }
     }
-    if (gb_next < a.NB) {
-      const char* vb =
-          (const char*)(a.vt + ((size_t)gb_next * a.H + h) * D * (size_t)a.block_size + off_next);
+    const int gb = min(gb_next, a.NB - 1);
+    const char* vb = (const char*)(a.vt + ((size_t)gb * a.H + h) * D * (size_t)a.block_size + off_next);
+    char* vl = kl + KBYTES;
 #pragma unroll
-      for (int i = 0; i < VSEG; ++i) vbuf[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VSEG; ++i) vbuf[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < VIW; ++i) {
+      const int j = w + kWaves * i;
+      if (NVI % kWaves == 0 || j < NVI)
+        lds_dma16(vb + voff[i], vl + j * 1024);
     }
     off_next += kTK;
     if (off_next == a.block_size) { off_next = 0; ++gb_next; }
   };
-  auto store_chunk = [&](int buf) {
+
+  // ---------------- LDS operand addresses ----------------
+  // K fragment (32 sc + l32, 16 ks + 8 hf): the row's swizzle depends on l32 only
+  uint32_t kaddr[KS], vaddr[2][2];
 #pragma unroll
-    for (int i = 0; i < KSEG; ++i) {
-      const int seg = tid + kThreads * i;
-      if (NSEG % kThreads == 0 || seg < NSEG) {
-        const int r = seg / (D / 8), c = seg % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][r * KROW + c * 8]) = kbuf[i];
-      }
-    }
+  for (int ks = 0; ks < KS; ++ks)
+    kaddr[ks] = (uint32_t)(l32 * KRB + (((2 * ks + hf) ^ swz<KRB>(l32)) << 4));
+  // V^T fragment (row 32 dt + l32, keys 32 sc + 16 mm + 8 hf)
 #pragma unroll
-    for (int i = 0; i < VSEG; ++i) {
-      const int seg = tid + kThreads * i;
-      if (NSEG % kThreads == 0 || seg < NSEG) {
-        const int r = seg / (kTK / 8), c = seg % (kTK / 8);
-        *reinterpret_cast<u32x4*>(&Vs[buf][r * VROW + c * 8]) = vbuf[i];
-      }
-    }
-  };
+  for (int sc = 0; sc < 2; ++sc)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+      vaddr[sc][mm] = (uint32_t)(KBYTES + l32 * VRB + (((4 * sc + 2 * mm + hf) ^ swz<VRB>(l32)) << 4));
 
   // ---------------- main loop ----------------
-  // Software pipeline over 32-key steps: the QK^T product of the next step is
-  // issued while the probabilities of the current step are formed, and the
-  // current PV product runs while the next step's row max is taken, so the
-  // matrix cores and the vector ALUs of a wave work side by side.
-  static_assert(QT == 1, "one 32-query column tile per wave");
   f32x16 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -248,17 +251,17 @@ void attn_mfma_kernel(MfmaArgs a) {
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
   float m_use = -INFINITY, l_run = 0.f;
   const float scale2 = a.scale2;
-  const int qp = qpos[0];
 
-  auto qk = [&](int buf, int sc) {
+  auto qk = [&](const char* base, int sc) {
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(base + kaddr[ks] + sc * 32 * KRB);
     f32x16 S;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * sc + l32) * KROW + 16 * ks + 8 * hf]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[0][ks], S, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], S, 0, 0, 0);
     return S;
   };
   // S[r] is the score of query column (lane & 31) with key kp + 8 (r / 4) + 4 hf + (r % 4)
@@ -266,30 +269,10 @@ void attn_mfma_kernel(MfmaArgs a) {
     if (MODE != kModeHist && kp + 31 > wq_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kp + 8 * (r >> 2) + 4 * hf + (r & 3) > qp) S[r] = -INFINITY;
+        if (kp + 8 * (r >> 2) + 4 * hf + (r & 3) > qpos) S[r] = -INFINITY;
     }
   };
-  auto row_max = [&](const f32x16& S) {
-    float mx = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    return max_with_partner(mx);
-  };
-  auto rescale = [&](float mx) {
-    const float cand = mx * scale2;
-    if (__ballot(cand > m_use + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_use, cand);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
-      m_use = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-    }
-  };
-  auto probs = [&](f32x16 S, f16x8* P) {
-    const float base = m_use == -INFINITY ? 0.f : m_use;
+  auto probs = [&](f32x16 S, f16x8* P, float base) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale2, -base));
 #pragma unroll
@@ -301,93 +284,88 @@ void attn_mfma_kernel(MfmaArgs a) {
     for (int r = 0; r < 16; ++r) ls += S[r];
     l_run += ls;
   };
-  auto pv = [&](int buf, int sc, const f16x8* P) {
+  auto pv = [&](const char* base, int sc, const f16x8* P) {
+    f16x8 vf[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(&Vs[buf][(32 * dt + l32) * VROW + 32 * sc + 16 * mm + 8 * hf]);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, P[mm], O[dt], 0, 0, 0);
-      }
+      for (int mm = 0; mm < 2; ++mm)
+        vf[dt][mm] = *reinterpret_cast<const f16x8*>(base + vaddr[sc][mm] + dt * 32 * VRB);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][mm], P[mm], O[dt], 0, 0, 0);
   };
 
-  load_chunk(0);
-  store_chunk(0);
-  if (nchunks > 1) load_chunk(1);
+  load_chunk(0, 0);
   __syncthreads();
-  f32x16 Sa = qk(0, 0);
-  mask(Sa, key_lo);
-  rescale(row_max(Sa));
   for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
+    const char* base = smem + (c & 1) * BUF;
+    if (c + 1 < nchunks) load_chunk(c + 1, (c + 1) & 1);
     const int kp0 = key_lo + c * kTK;
-    f16x8 P[2];
-    // first 32 keys of chunk c; the QK^T of its second 32 keys is in flight
-    f32x16 Sb = qk(buf, 1);
-    probs(Sa, P);
-    pv(buf, 0, P);
-    mask(Sb, kp0 + 32);
-    const float mxb = row_max(Sb);
-    if (c + 1 < nchunks) store_chunk(buf ^ 1);
-    __syncthreads();  // chunk c + 1 is in LDS
-    if (c + 2 < nchunks) load_chunk(c + 2);
-    rescale(mxb);
-    // second 32 keys of chunk c; the QK^T of chunk c + 1's first 32 keys is in
-    // flight (on the last chunk it reads a stale buffer and is discarded)
-    Sa = qk(buf ^ 1, 0);
-    probs(Sb, P);
-    pv(buf, 1, P);
-    if (c + 1 < nchunks) {
-      mask(Sa, kp0 + kTK);
-      rescale(row_max(Sa));
+    f32x16 S0 = qk(base, 0);
+    f32x16 S1 = qk(base, 1);
+    mask(S0, kp0);
+    mask(S1, kp0 + 32);
+    float mx = S0[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+    const float cand = max_with_partner(mx) * scale2;
+    if (__ballot(cand > m_use + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_use, cand);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
+      m_use = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
     }
-    __syncthreads();  // every wave is done with chunk c's buffer
+    const float ebase = m_use == -INFINITY ? 0.f : m_use;
+    f16x8 P0[2], P1[2];
+    probs(S0, P0, ebase);
+    pv(base, 0, P0);
+    probs(S1, P1, ebase);
+    pv(base, 1, P1);
+    __syncthreads();  // chunk c + 1 has landed; everyone is done with chunk c
   }
 
   // ---------------- epilogue ----------------
+  if (qtok < 0) return;  // both lanes of a query column take the same branch
   float out_scale = 1.f;
   if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
-  {
-    constexpr int qt = 0;
-    // both lanes of a query column take the same branch
-    if (qtok[qt] < 0) return;
-    const float l_tot = sum_with_partner(l_run);
-    const float inv = out_scale / l_tot;
-    const float lse_val = (m_use + log2f(l_tot)) * kLn2;
-    // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
-    if (MODE == kModeDense && !OUT_BF16) {
-      float* op = (float*)a.o_out + (size_t)oidx[qt] * D;
+  const float l_tot = sum_with_partner(l_run);
+  const float inv = out_scale / l_tot;
+  const float lse_val = (m_use + log2f(l_tot)) * kLn2;
+  // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
+  if (MODE == kModeDense && !OUT_BF16) {
+    float* op = (float*)a.o_out + (size_t)oidx * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv,
-                      O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
-        }
-    } else if (MODE == kModeDense) {
-      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx[qt] * D;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv, O[dt][4 * g + 2] * inv,
+                    O[dt][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
+      }
+  } else {
+    uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 v2 = {pack_bf16x2(O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv),
-                      pack_bf16x2(O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
-        }
-    } else {
-      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx[qt] * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 v2 = {pack_f16x2(O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv),
-                      pack_f16x2(O[dt][4 * g + 2] * inv, O[dt][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
-        }
-    }
-    if (hf == 0) a.lse_out[oidx[qt]] = lse_val;
+      for (int g = 0; g < 4; ++g) {
+        const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
+        const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
+        u32x2 v2;
+        if (MODE == kModeDense) v2 = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        else v2 = u32x2{pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+      }
   }
+  if (hf == 0) a.lse_out[oidx] = lse_val;
 }
 
 static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, const Geo& g,
@@ -420,9 +398,9 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
   a.lse_out = lse_part;
   dim3 grid((unsigned)max_tiles);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true, kQT>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true, kQT>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -437,9 +415,9 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
   a.lse_out = lse_part;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.num_heads);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true, kQT>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true, kQT>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -455,7 +433,7 @@ hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* 
   a.lse_out = lse;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.num_heads);
 #define MOBA_DENSE(D, OB) \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB, kQT>), grid, dim3(kThreads), 0, st, a)
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB>), grid, dim3(kThreads), 0, st, a)
   if (g.head_dim == 128) { if (out_bf16) MOBA_DENSE(128, true); else MOBA_DENSE(128, false); }
   else { if (out_bf16) MOBA_DENSE(64, true); else MOBA_DENSE(64, false); }
 #undef MOBA_DENSE
