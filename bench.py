@@ -48,6 +48,10 @@ def dense_pairs(seqlens, H):
     return H * sum(L * (L + 1) // 2 for L in seqlens)
 
 
+# sources the historical-attention kernel is built from
+HIST_SOURCES = ("attn_mfma.hip", "common.h", "launch.h")
+
+
 def kernel_source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -56,15 +60,16 @@ def kernel_source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, kernel_file):
-    """HBM bytes per launch of the dominant kernel from a committed counter
-    summary, if it was taken on the current kernel source; else None."""
+def traffic_from_profiles(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration),
+    if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"attn_hist_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash(kernel_file, "common.h"):
+    if rec.get("source_hash") != kernel_source_hash(*HIST_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -141,6 +146,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -151,6 +158,18 @@ def main():
 
     import torch
     from block_sparse_long_03_amd import inputs, moba
+
+    if args.copy_probe:
+        # a plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of this
+        # kernel calibrate the counters against 4 GiB read + 4 GiB written
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 4 * n, "launches": 3}))
+        return
 
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -224,7 +243,7 @@ def main():
     avg_h = ms_h / max(n_h, 1)
     hist_flops = 4.0 * d * hist_p
     achieved = hist_flops / (avg_h * 1e-3) / 1e12 if avg_h > 0 else 0.0
-    traffic = traffic_from_profiles(w.name, "attn_mfma.hip")
+    traffic = traffic_from_profiles(w.name)
     roofline = {"kernel": "attn_hist (attn_mfma_kernel, historical blocks)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
