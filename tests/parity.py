@@ -10,6 +10,9 @@ log-sum-exp within 1e-3 absolute.  fp32 inputs: 1e-4 on outputs and lse.
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -53,7 +56,21 @@ def error_stats(o_gpu, o_ref, lse_gpu, lse_ref):
                 if diff.size else 0.0)
 
 
+def emit(stats):
+    """Prints the error statistics of the running test and, when the
+    environment names a file in MOBA_PARITY_REPORT, appends them there as one
+    JSON line."""
+    name = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    line = json.dumps({"test": name, **stats})
+    print("[stats]", line, flush=True)
+    path = os.environ.get("MOBA_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
 def assert_within(stats, tol, what=""):
+    emit(stats)
     for key in ("max_abs", "rel_l2", "lse_abs"):
         assert stats[key] <= tol[key], f"{what}: {key} {stats[key]:.3e} > {tol[key]:.1e} ({stats})"
 
@@ -98,4 +115,6 @@ def check_idx_all_rows(q, k, cu, B, topk, idx, heads=None):
         sel = check_selection(q_h, k_h, cu, B, topk, rows_h, idx_g)
         n_near += sel["n_near"]
         n_mis += sel["n_mismatch"]
-    return dict(n_near=n_near, n_mismatch=n_mis)
+    st = dict(n_near=n_near, n_mismatch=n_mis, rows=int(T) * (H if heads is None else len(heads)))
+    emit(st)
+    return st
