@@ -28,6 +28,8 @@
 // XOR-swizzled in 16-byte segments so that the MFMA operand reads are free of
 // bank conflicts: rows of 256 B use segment ^ (row & 15), rows of 128 B use
 // segment ^ ((row >> 1) & 7).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -107,7 +109,7 @@ void attn_mfma_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -180,68 +182,78 @@ void attn_mfma_kernel(MfmaArgs a) {
   }
 
   // ---------------- chunk loads (global -> LDS) ----------------
+  // Wave instruction i of a chunk load fills LDS bytes [(w + kWaves i) KiB,
+  // +1 KiB): lane `lane` writes 16 bytes of row r at segment lseg.  Moving
+  // to the next instruction adds a whole number of 16-row groups, so the
+  // swizzle, and with it the lane's source offset, only shifts by a uniform
+  // amount.
+  constexpr int KROWS_I = kWaves * 1024 / KRB;  // K rows per wave instruction step
+  constexpr int VROWS_I = kWaves * 1024 / VRB;
+  static_assert(KROWS_I % 16 == 0 && VROWS_I % 16 == 0, "uniform per-instruction offsets");
   const int nchunks = (key_hi - key_lo + kTK - 1) / kTK;
   const size_t krow_bytes = (size_t)a.H * D * 2;
   const char* kseq = (const char*)a.k + ((size_t)seq_start * a.H + h) * D * 2;
-  int krow[KIW];
-  uint32_t koff[KIW], voff[VIW];
-#pragma unroll
-  for (int i = 0; i < KIW; ++i) {
-    const int L = (w + kWaves * i) * 1024 + lane * 16;  // LDS byte this lane fills
-    const int r = L / KRB;
-    const int lseg = ((L % KRB) >> 4) ^ swz<KRB>(r);
-    krow[i] = r;
-    koff[i] = (uint32_t)(r * krow_bytes + lseg * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < VIW; ++i) {
-    const int L = (w + kWaves * i) * 1024 + lane * 16;
-    const int r = L / VRB;
-    const int lseg = ((L % VRB) >> 4) ^ swz<VRB>(r);
-    voff[i] = (uint32_t)(r * a.block_size * 2 + lseg * 16);
-  }
-  int gb_next = gb_base + key_lo / a.block_size;  // V^T source of the next chunk
-  int off_next = key_lo % a.block_size;
-  auto load_chunk = [&](int ch, int buf) {
+  const int krow0 = (w * 1024 + lane * 16) / KRB;
+  const uint32_t koff0 = (uint32_t)(krow0 * krow_bytes +
+                                    ((((lane * 16) % KRB) >> 4) ^ swz<KRB>(krow0)) * 16);
+  const int vrow0 = (w * 1024 + lane * 16) / VRB;
+  const uint32_t voff0 = (uint32_t)(vrow0 * a.block_size * 2 +
+                                    ((((lane * 16) % VRB) >> 4) ^ swz<VRB>(vrow0)) * 16);
+  // K rows of chunk ch into slot buf; rows past the sequence end repeat its
+  // last key (they are always masked)
+  auto load_k = [&](int ch, int buf) {
     const int kp0 = key_lo + ch * kTK;
     char* kl = smem + buf * BUF;
     const char* kb = kseq + (size_t)kp0 * krow_bytes;
-    const bool full = kp0 + kTK <= seq_len;
+    if (kp0 + kTK <= seq_len) {
 #pragma unroll
-    for (int i = 0; i < KIW; ++i) {
-      const int j = w + kWaves * i;
-      if (NKI % kWaves == 0 || j < NKI) {
-        // rows past the sequence end repeat its last key (always masked)
-        const char* src = full ? kb + koff[i]
-                               : kb + koff[i] - (size_t)max(0, kp0 + krow[i] - (seq_len - 1)) * krow_bytes;
-        lds_dma16(src, kl + j * 1024);
+      for (int i = 0; i < KIW; ++i) {
+        const int j = w + kWaves * i;
+        if (NKI % kWaves == 0 || j < NKI)
+          lds_dma16(kb + (size_t)i * KROWS_I * krow_bytes + koff0, kl + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KIW; ++i) {
+        const int j = w + kWaves * i;
+        const int over = max(0, kp0 + krow0 + i * KROWS_I - (seq_len - 1));
+        if (NKI % kWaves == 0 || j < NKI)
+          lds_dma16(kb + (size_t)(i * KROWS_I - over) * krow_bytes + koff0, kl + j * 1024);
       }
     }
+  };
+  // V^T columns of the next chunk in order (staged per block: block gb_next,
+  // key offset off_next inside it)
+  int gb_next = gb_base + key_lo / a.block_size;
+  int off_next = key_lo % a.block_size;
+  auto load_v = [&](int buf) {
     const int gb = min(gb_next, a.NB - 1);
     const char* vb = (const char*)(a.vt + ((size_t)gb * a.H + h) * D * (size_t)a.block_size + off_next);
-    char* vl = kl + KBYTES;
+    char* vl = smem + buf * BUF + KBYTES;
 #pragma unroll
     for (int i = 0; i < VIW; ++i) {
       const int j = w + kWaves * i;
       if (NVI % kWaves == 0 || j < NVI)
-        lds_dma16(vb + voff[i], vl + j * 1024);
+        lds_dma16(vb + (size_t)i * VROWS_I * a.block_size * 2 + voff0, vl + j * 1024);
     }
     off_next += kTK;
     if (off_next == a.block_size) { off_next = 0; ++gb_next; }
   };
 
   // ---------------- LDS operand addresses ----------------
-  // K fragment (32 sc + l32, 16 ks + 8 hf): the row's swizzle depends on l32 only
-  uint32_t kaddr[KS], vaddr[2][2];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    kaddr[ks] = (uint32_t)(l32 * KRB + (((2 * ks + hf) ^ swz<KRB>(l32)) << 4));
-  // V^T fragment (row 32 dt + l32, keys 32 sc + 16 mm + 8 hf)
-#pragma unroll
-  for (int sc = 0; sc < 2; ++sc)
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-      vaddr[sc][mm] = (uint32_t)(KBYTES + l32 * VRB + (((4 * sc + 2 * mm + hf) ^ swz<VRB>(l32)) << 4));
+  // K fragment (row 32 sc + l32, dims 16 ks + 8 hf) sits at segment
+  // (2 ks + hf) ^ swz(l32) of its row, i.e. at kbase0 ^ (ks << 5); V^T fragment
+  // (row 32 dt + l32, keys 32 sc + 16 mm + 8 hf) at vbase0 ^ ((2 sc + mm) << 5)
+  // + dt * 32 rows.  The per-step XOR is recomputed at each use (one VALU op)
+  // rather than holding twelve address registers.
+  const uint32_t kbase0 = (uint32_t)(l32 * KRB + ((hf ^ swz<KRB>(l32)) << 4));
+  const uint32_t vbase0 = (uint32_t)(KBYTES + l32 * VRB + ((hf ^ swz<VRB>(l32)) << 4));
+  auto kfrag = [&](uint32_t kb, int slot, int sc, int ks) {
+    return *reinterpret_cast<const bf16x8*>(smem + slot * BUF + sc * 32 * KRB + (kb ^ (ks << 5)));
+  };
+  auto vfrag = [&](uint32_t vb, int slot, int j, int dt) {
+    return *reinterpret_cast<const f16x8*>(smem + slot * BUF + dt * 32 * VRB + (vb ^ (j << 5)));
+  };
 
   // ---------------- main loop ----------------
   f32x16 O[DT];
@@ -252,18 +264,6 @@ void attn_mfma_kernel(MfmaArgs a) {
   float m_use = -INFINITY, l_run = 0.f;
   const float scale2 = a.scale2;
 
-  auto qk = [&](const char* base, int sc) {
-    bf16x8 kf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8*>(base + kaddr[ks] + sc * 32 * KRB);
-    f32x16 S;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], S, 0, 0, 0);
-    return S;
-  };
   // S[r] is the score of query column (lane & 31) with key kp + 8 (r / 4) + 4 hf + (r % 4)
   auto mask = [&](f32x16& S, int kp) {
     if (MODE != kModeHist && kp + 31 > wq_min) {
@@ -272,65 +272,173 @@ void attn_mfma_kernel(MfmaArgs a) {
         if (kp + 8 * (r >> 2) + 4 * hf + (r & 3) > qpos) S[r] = -INFINITY;
     }
   };
-  auto probs = [&](f32x16 S, f16x8* P, float base) {
+  auto qk = [&](uint32_t kb, int slot, int sc) {
+    f32x16 S;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale2, -base));
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) P[mm][i] = (_Float16)S[8 * mm + i];
-    float ls = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ls += S[r];
-    l_run += ls;
+    for (int ks = 0; ks < KS; ++ks)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kb, slot, sc, ks), qreg[ks], S, 0, 0, 0);
+    return S;
   };
-  auto pv = [&](const char* base, int sc, const f16x8* P) {
-    f16x8 vf[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-        vf[dt][mm] = *reinterpret_cast<const f16x8*>(base + vaddr[sc][mm] + dt * 32 * VRB);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][mm], P[mm], O[dt], 0, 0, 0);
+  // keeps the fragment bases from being hoisted and expanded into one
+  // register per step
+  auto opaque = [](uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
   };
 
-  load_chunk(0, 0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const char* base = smem + (c & 1) * BUF;
-    if (c + 1 < nchunks) load_chunk(c + 1, (c + 1) & 1);
+  // Software pipeline over 64-key chunks, scheduled by hand: in-order issue
+  // means a VALU instruction placed between two MFMAs runs while the first
+  // is in the matrix pipe, so each MFMA below is followed by a slice of the
+  // softmax arithmetic, and by the LDS read of the operand three MFMAs
+  // ahead; sched_barrier fences keep the compiler from regrouping them.
+  //   A: QK^T(c + 1, keys 0-31)  with  t = s * scale * log2(e) - base and the
+  //      row max of chunk c (base: the running max before this chunk);
+  //   rescale (rare: the max grew by more than kRescaleSlack);
+  //   B: QK^T(c + 1, keys 32-63) with  exp2 of t for keys 0-31,
+  //      PV(c, keys 0-31)        with  exp2 of t for keys 32-63,
+  //      PV(c, keys 32-63).
+  // K and V^T have separate double buffers (slot = chunk parity): iteration
+  // c reads K(c + 1) and V(c) and fills K(c + 2) and V(c + 1).
+  constexpr int NPV = DT * 2;       // MFMAs of one 32-key PV step
+  constexpr int PF = 3;             // LDS operand prefetch distance (MFMAs)
+  constexpr int EA = 32 / KS;       // scores scaled per MFMA in A
+  constexpr int EB = 16 / KS;       // probabilities per MFMA in QK part of B
+  constexpr int EP = 16 / NPV;      // probabilities per MFMA in PV part of B
+  static_assert(KS >= PF && NPV >= PF, "prefetch distance");
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // probabilities e = exp2(t) of values [v0, v0 + n) of T: rounded to fp16
+  // into P, summed in fp32 into l_run
+  auto probs_part = [&](const f32x16& T, f16x8* P, int v0, int n) {
+#pragma unroll
+    for (int v = v0; v < v0 + n; v += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(T[v]);
+      const float e1 = __builtin_amdgcn_exp2f(T[v + 1]);
+      P[v >> 3][v & 7] = (_Float16)e0;
+      P[v >> 3][(v + 1) & 7] = (_Float16)e1;
+      l_run += e0 + e1;
+    }
+  };
+  auto iteration = [&](int c, f32x16& S0, f32x16& S1, f32x16& N0, f32x16& N1, auto odd_t,
+                       auto more_t) {
+    constexpr int CS = decltype(odd_t)::value ? 1 : 0;  // slot of chunk c
+    constexpr int NS = CS ^ 1;                           // slot of chunk c + 1
+    constexpr bool MORE = decltype(more_t)::value;
     const int kp0 = key_lo + c * kTK;
-    f32x16 S0 = qk(base, 0);
-    f32x16 S1 = qk(base, 1);
     mask(S0, kp0);
     mask(S1, kp0 + 32);
-    float mx = S0[0];
+    if (c + 2 < nchunks) load_k(c + 2, CS);
+    if (MORE) load_v(NS);
+    const uint32_t kb = opaque(kbase0);
+    const uint32_t vb = opaque(vbase0);
+    const float base_old = m_use == -INFINITY ? 0.f : m_use;
+    bf16x8 kf[KS], kg[KS];
+    f16x8 vf[NPV], vg[NPV];
+    auto vread = [&](f16x8* dst, int sc, int i) {
+      dst[i] = vfrag(vb, CS, 2 * sc + i / DT, i % DT);
+    };
+    // ---- A
+    float mx = -INFINITY;
+    if (MORE) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+      for (int ks = 0; ks < PF; ++ks) kf[ks] = kfrag(kb, NS, 0, ks);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
-    const float cand = max_with_partner(mx) * scale2;
-    if (__ballot(cand > m_use + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_use, cand);
+      for (int r = 0; r < 16; ++r) N0[r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fence();
+      if (MORE) {
+        N0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], N0, 0, 0, 0);
+        if (ks + PF < KS) kf[ks + PF] = kfrag(kb, NS, 0, ks + PF);
+        else kg[ks + PF - KS] = kfrag(kb, NS, 1, ks + PF - KS);
+      }
+#pragma unroll
+      for (int v = ks * EA; v < (ks + 1) * EA; v += 2) {
+        f32x16& T = v < 16 ? S0 : S1;
+        const int r = v & 15;
+        T[r] = fmaf(T[r], scale2, -base_old);
+        T[r + 1] = fmaf(T[r + 1], scale2, -base_old);
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(T[r], T[r + 1]));
+      }
+    }
+    fence();
+    const float cand = max_with_partner(mx);  // in units of t: max(s) * scale2 - base_old
+    if (__ballot(cand > (m_use == -INFINITY ? -INFINITY : kRescaleSlack)) != 0) {
+      const float m_new = fmaxf(m_use, base_old + cand);
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
+      const float delta = (m_new == -INFINITY ? 0.f : m_new) - base_old;
       m_use = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S0[r] -= delta;
+        S1[r] -= delta;
+      }
     }
-    const float ebase = m_use == -INFINITY ? 0.f : m_use;
+    // ---- B
+    const uint32_t kb2 = opaque(kbase0);
     f16x8 P0[2], P1[2];
-    probs(S0, P0, ebase);
-    pv(base, 0, P0);
-    probs(S1, P1, ebase);
-    pv(base, 1, P1);
-    __syncthreads();  // chunk c + 1 has landed; everyone is done with chunk c
+    if (MORE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) N1[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        fence();
+        N1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kg[ks], qreg[ks], N1, 0, 0, 0);
+        if (ks + PF < KS) kg[ks + PF] = kfrag(kb2, NS, 1, ks + PF);
+        else vread(vf, 0, ks + PF - KS);
+        probs_part(S0, P0, ks * EB, EB);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) vread(vf, 0, i);
+      probs_part(S0, P0, 0, 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      fence();
+      O[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i], P0[i / DT], O[i % DT], 0, 0, 0);
+      if (i + PF < NPV) vread(vf, 0, i + PF);
+      else vread(vg, 1, i + PF - NPV);
+      probs_part(S1, P1, i * EP, EP);
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      fence();
+      O[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vg[i], P1[i / DT], O[i % DT], 0, 0, 0);
+      if (i + PF < NPV) vread(vg, 1, i + PF);
+    }
+    fence();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  load_k(0, 0);
+  load_v(0);
+  if (nchunks > 1) load_k(1, 1);
+  __syncthreads();
+  f32x16 S0 = qk(kbase0, 0, 0);
+  f32x16 S1 = qk(kbase0, 0, 1);
+  f32x16 N0, N1;
+  __syncthreads();  // K(0) is read: its slot takes K(2)
+  int c = 0;
+  for (; c + 2 < nchunks; c += 2) {
+    iteration(c, S0, S1, N0, N1, no(), yes());
+    __syncthreads();  // K(c + 2) and V(c + 1) have landed; K(c + 1) and V(c) are read
+    iteration(c + 1, N0, N1, S0, S1, yes(), yes());
+    __syncthreads();
+  }
+  if (c + 1 < nchunks) {
+    iteration(c, S0, S1, N0, N1, no(), yes());
+    __syncthreads();
+    iteration(c + 1, N0, N1, S0, S1, yes(), no());
+  } else {
+    iteration(c, S0, S1, N0, N1, no(), no());
   }
 
   // ---------------- epilogue ----------------
