@@ -135,10 +135,14 @@ void attn_mfma_kernel(MfmaArgs a) {
       oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
     }
   } else {
-    h = blockIdx.y;
+    // XCD-contiguous order: the tiles of one block (own) or sequence (dense)
+    // and head share an L2
+    const int L = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+    const int bx = L % gridDim.x;
+    h = L / gridDim.x;
     const int per_seq = a.tiles_per_unit * a.units_per_seq;
-    const int s = blockIdx.x / per_seq;
-    const int rem = per_seq - 1 - (int)(blockIdx.x % per_seq);  // heavy tiles first
+    const int s = bx / per_seq;
+    const int rem = per_seq - 1 - (bx % per_seq);  // heavy tiles first
     seq_span(a.cu_seqlens, s, a.total_tokens, &seq_start, &seq_len);
     gb_base = a.cu_blocks[s];
     int q_lo, q_hi;
@@ -302,7 +306,7 @@ void attn_mfma_kernel(MfmaArgs a) {
   // K and V^T have separate double buffers (slot = chunk parity): iteration
   // c reads K(c + 1) and V(c) and fills K(c + 2) and V(c + 1).
   constexpr int NPV = DT * 2;       // MFMAs of one 32-key PV step
-  constexpr int PF = 3;             // LDS operand prefetch distance (MFMAs)
+  constexpr int PF = MOBA_ATTN_PF < KS ? MOBA_ATTN_PF : KS;  // LDS operand prefetch distance (MFMAs)
   constexpr int EA = 32 / KS;       // scores scaled per MFMA in A
   constexpr int EB = 16 / KS;       // probabilities per MFMA in QK part of B
   constexpr int EP = 16 / NPV;      // probabilities per MFMA in PV part of B

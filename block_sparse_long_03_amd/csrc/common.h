@@ -101,6 +101,16 @@ __device__ __forceinline__ int count_hist(const int32_t* __restrict__ row, int t
   return nh;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2): workgroup b runs on XCD b % 8.  xcd_remap(b, n) gives workgroup b the
+// work item that makes every XCD process one contiguous share of [0, n), so
+// neighbouring work items (which read the same K/V blocks) share an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b % kXcds, j = b / kXcds;
+  return x * (n / kXcds) + min(x, n % kXcds) + j;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

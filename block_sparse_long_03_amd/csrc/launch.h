@@ -32,6 +32,9 @@ struct Geo {
 #ifndef MOBA_ATTN_OCC
 #define MOBA_ATTN_OCC 2  // target waves per SIMD (bounds the kernels' registers)
 #endif
+#ifndef MOBA_ATTN_PF
+#define MOBA_ATTN_PF 3  // LDS operand prefetch distance of the MFMA attention loop
+#endif
 constexpr int kMfmaWaves = MOBA_ATTN_WAVES;
 constexpr int kMfmaWavesPerSimd = MOBA_ATTN_OCC;
 constexpr int kMfmaTileQ = 32 * MOBA_ATTN_WAVES * MOBA_ATTN_QT;
