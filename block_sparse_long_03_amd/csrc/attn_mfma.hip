@@ -68,9 +68,6 @@ struct MfmaArgs {
 };
 
 constexpr int kTK = 64;     // keys per LDS chunk
-constexpr int kWaves = kMfmaWaves;
-constexpr int kThreads = 64 * kWaves;
-static_assert(kMfmaTileQ == kWaves * 32, "one 32-query column tile per wave");
 
 // segment swizzle of an LDS tile row (row_bytes 256 or 128)
 template <int ROW_BYTES>
@@ -90,8 +87,8 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
 // rarely; probabilities stay below 256 (exact in the final normalisation).
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerSimd)))
+template <int D, int MODE, bool OUT_BF16, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerSimd)))
 void attn_mfma_kernel(MfmaArgs a) {
   constexpr int TQ = kWaves * 32;
   constexpr int KS = D / 16;             // MFMA k-steps of the QK^T product
@@ -306,7 +303,7 @@ void attn_mfma_kernel(MfmaArgs a) {
   // K and V^T have separate double buffers (slot = chunk parity): iteration
   // c reads K(c + 1) and V(c) and fills K(c + 2) and V(c + 1).
   constexpr int NPV = DT * 2;       // MFMAs of one 32-key PV step
-  constexpr int PF = MOBA_ATTN_PF < KS ? MOBA_ATTN_PF : KS;  // LDS operand prefetch distance (MFMAs)
+  constexpr int PF = 3;             // LDS operand prefetch distance (MFMAs)
   constexpr int EA = 32 / KS;       // scores scaled per MFMA in A
   constexpr int EB = 16 / KS;       // probabilities per MFMA in QK part of B
   constexpr int EP = 16 / NPV;      // probabilities per MFMA in PV part of B
@@ -498,6 +495,14 @@ static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, cons
   return a;
 }
 
+template <int D, int MODE, bool OB>
+static void launch_mfma(int waves, dim3 grid, hipStream_t st, const MfmaArgs& a) {
+  if (waves == 8)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, OB, 8>), grid, dim3(64 * 8), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, OB, 4>), grid, dim3(64 * 4), 0, st, a);
+}
+
 hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* vt,
                                  const Geo& g, int topk, float scale, const int32_t* list,
                                  const int4* tile_info, long long max_tiles, uint16_t* o_part,
@@ -508,11 +513,11 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
   a.tile_info = tile_info;
   a.o_out = o_part;
   a.lse_out = lse_part;
+  // tile_info was cut into tiles of mfma_tile_q(block_size) queries
+  const int waves = mfma_waves(g.block_size);
   dim3 grid((unsigned)max_tiles);
-  if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHist, true>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHist, true>), grid, dim3(kThreads), 0, st, a);
+  if (g.head_dim == 128) launch_mfma<128, kModeHist, true>(waves, grid, st, a);
+  else launch_mfma<64, kModeHist, true>(waves, grid, st, a);
   return hipGetLastError();
 }
 
@@ -521,15 +526,15 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
                                 float* lse_part, hipStream_t st) {
   if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, topk, scale);
-  a.tiles_per_unit = (g.block_size + kMfmaTileQ - 1) / kMfmaTileQ;
+  // own-block tiles span at most one block of keys: 4 waves
+  const int waves = 4;
+  a.tiles_per_unit = (g.block_size + 32 * waves - 1) / (32 * waves);
   a.units_per_seq = (g.max_seqlen + g.block_size - 1) / g.block_size;
   a.o_out = o_part;
   a.lse_out = lse_part;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.num_heads);
-  if (g.head_dim == 128)
-    hipLaunchKernelGGL((attn_mfma_kernel<128, kModeOwn, true>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<64, kModeOwn, true>), grid, dim3(kThreads), 0, st, a);
+  if (g.head_dim == 128) launch_mfma<128, kModeOwn, true>(waves, grid, st, a);
+  else launch_mfma<64, kModeOwn, true>(waves, grid, st, a);
   return hipGetLastError();
 }
 
@@ -539,16 +544,19 @@ hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* 
   if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, 1, scale);
   a.vmax_bits = vmax_bits;
-  a.tiles_per_unit = (g.max_seqlen + kMfmaTileQ - 1) / kMfmaTileQ;
+  const int waves = mfma_waves(g.max_seqlen);
+  a.tiles_per_unit = (g.max_seqlen + 32 * waves - 1) / (32 * waves);
   a.units_per_seq = 1;
   a.o_out = out;
   a.lse_out = lse;
   dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.num_heads);
-#define MOBA_DENSE(D, OB) \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kModeDense, OB>), grid, dim3(kThreads), 0, st, a)
-  if (g.head_dim == 128) { if (out_bf16) MOBA_DENSE(128, true); else MOBA_DENSE(128, false); }
-  else { if (out_bf16) MOBA_DENSE(64, true); else MOBA_DENSE(64, false); }
-#undef MOBA_DENSE
+  if (g.head_dim == 128) {
+    if (out_bf16) launch_mfma<128, kModeDense, true>(waves, grid, st, a);
+    else launch_mfma<128, kModeDense, false>(waves, grid, st, a);
+  } else {
+    if (out_bf16) launch_mfma<64, kModeDense, true>(waves, grid, st, a);
+    else launch_mfma<64, kModeDense, false>(waves, grid, st, a);
+  }
   return hipGetLastError();
 }
 

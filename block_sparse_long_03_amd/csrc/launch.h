@@ -20,24 +20,14 @@ struct Geo {
   int block_size;
 };
 
-// Query tile (rows per workgroup) of the bf16 MFMA attention kernels and of
-// the fp32 attention kernels; the bucket scan cuts the per-block query lists
-// into tiles of this many rows.
-#ifndef MOBA_ATTN_QT
-#define MOBA_ATTN_QT 1  // 32-query column tiles per wave of the MFMA attention kernels
-#endif
-#ifndef MOBA_ATTN_WAVES
-#define MOBA_ATTN_WAVES 4  // waves per workgroup of the MFMA attention kernels
-#endif
-#ifndef MOBA_ATTN_OCC
-#define MOBA_ATTN_OCC 2  // target waves per SIMD (bounds the kernels' registers)
-#endif
-#ifndef MOBA_ATTN_PF
-#define MOBA_ATTN_PF 3  // LDS operand prefetch distance of the MFMA attention loop
-#endif
-constexpr int kMfmaWaves = MOBA_ATTN_WAVES;
-constexpr int kMfmaWavesPerSimd = MOBA_ATTN_OCC;
-constexpr int kMfmaTileQ = 32 * MOBA_ATTN_WAVES * MOBA_ATTN_QT;
+// Waves per workgroup of the MFMA attention kernels, one 32-query column
+// tile per wave.  Long key ranges (block size >= 1024) use 8 waves: one
+// 256-query tile per CU halves the K/V chunk traffic per flop.  Shorter ones
+// use 4 waves: two 128-query workgroups per CU hide each other's tile
+// start-up (list, query gather, first chunk).
+constexpr int kMfmaWavesPerSimd = 2;
+inline int mfma_waves(int key_range) { return key_range >= 1024 ? 8 : 4; }
+inline int mfma_tile_q(int key_range) { return 32 * mfma_waves(key_range); }
 constexpr int kF32TileQ = 1;
 
 // Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
@@ -47,9 +37,9 @@ struct AttnWorkspace {
 AttnWorkspace attn_workspace_layout(bool bf16, long long total_tokens, long long total_blocks,
                                     long long num_heads, long long head_dim,
                                     long long block_size, long long topk);
-// Upper bound on the number of historical tiles of kMfmaTileQ rows.
+// Upper bound on the number of historical tiles of mfma_tile_q(block_size) rows.
 long long hist_tiles_bound(long long total_tokens, long long total_blocks, long long num_heads,
-                           long long topk);
+                           long long block_size, long long topk);
 size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_heads,
                              long long head_dim, long long block_size);
 

@@ -142,6 +142,9 @@ EDGE = [
     inputs.custom([64 * 70 + 13], 2, 64, 64, 64, "bf16", name="d64-k64"),
     # fp32 with ragged tails and d = 128
     inputs.custom([300, 77, 512], 2, 128, 64, 3, "f32", name="f32-ragged"),
+    # block size >= 1024: 256-query historical tiles (8 waves), ragged tails
+    inputs.custom([3000, 2100, 700], 2, 128, 1024, 3, "bf16", name="B1024-ragged"),
+    inputs.custom([4100], 2, 64, 1024, 3, "bf16", name="d64-B1024"),
 ]
 
 
@@ -179,7 +182,8 @@ def test_moba_peaky_softmax(dev):
 
 
 def test_k_ge_n_matches_own_dense_kernel(dev):
-    w = inputs.custom([520, 1000], 2, 128, 128, 16, "bf16", name="k>n-vs-dense")
+    # the longest sequence reaches 1024 tokens: the dense kernel runs 8 waves
+    w = inputs.custom([520, 1100], 2, 128, 128, 16, "bf16", name="k>n-vs-dense")
     x, geom, out, lse, idx = _run(w, dev, seed=3, out_dtype=torch.float32)
     o_d, l_d = moba.dense(x["q"], x["k"], x["v"], geom, w.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -192,6 +196,7 @@ def test_k_ge_n_matches_own_dense_kernel(dev):
 @pytest.mark.parametrize("w", [
     inputs.custom([1000, 0, 64, 2000], 2, 128, 128, 2, "bf16", name="dense-varlen"),
     inputs.custom([900, 35], 2, 64, 64, 2, "bf16", name="dense-d64"),
+    inputs.custom([1500, 35], 2, 64, 64, 2, "bf16", name="dense-d64-long"),
     inputs.custom([300, 129], 2, 128, 64, 2, "f32", name="dense-f32"),
 ], ids=lambda w: w.name)
 def test_dense_causal(dev, w):
