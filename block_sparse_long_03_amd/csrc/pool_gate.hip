@@ -113,7 +113,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 constexpr int kGateRows = 64;    // query tokens per workgroup (they share one own block c)
 constexpr int kGateSpan = 256;   // past blocks per selection pass (4 per lane)
-constexpr int kGateChunk = 64;   // past blocks per scoring step
+constexpr int kGateStride = kGateSpan + 8;  // LDS row stride of the scores (8 banks apart)
+constexpr int kGateFastK = 16;   // k - 1 up to this: threshold from sorted per-lane lists
+constexpr int kGateChunk = 128;  // past blocks per MFMA scoring step (one 32 x 32 tile per wave)
+constexpr int kGateChunkValu = 64;  // past blocks per fp32 scoring step
 constexpr int kGateWaves = 8;
 constexpr int kGateRowsPerWave = kGateRows / kGateWaves;
 
@@ -127,32 +130,41 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r1 - m);  // at most 8 significant bits remain: exact
 }
 
-// Scores of a chunk of up to 64 past blocks for the 64 query rows, written to
-// ss[row][col0 + j].  bf16 queries: s = q . kbar with kbar split exactly into
-// three bf16 parts and the three products summed by v_mfma_f32_32x32x16_bf16
-// (products exact, fp32 accumulation); waves 0..3 each own one 32 x 32 tile.
+// Scores of a chunk of up to 128 past blocks for the 64 query rows, written
+// to ss[row][col0 + j].  bf16 queries: s = q . kbar with kbar split exactly
+// into three bf16 parts and the three products summed by
+// v_mfma_f32_32x32x16_bf16 (products exact, fp32 accumulation); each of the
+// 8 waves owns one 32 x 32 tile (token tile w / 4, block tile w % 4).
 template <int D>
 __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
                                                  const float* __restrict__ kbar, int H, int h,
                                                  int gblk0, int nb, int total_blocks,
-                                                 float (*ss)[kGateSpan + 1], int col0, int w,
+                                                 float (*ss)[kGateStride], int col0, int w,
                                                  int lane) {
-  if (w >= 4) return;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int bt = w & 1, tt = w >> 1;
+  const int bt = w & 3, tt = w >> 2;
   const int j = 32 * bt + l32;  // block of this lane's A rows
   const bool ok = j < nb && gblk0 + j < total_blocks;
-  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : 0) * H + h) * D + 8 * hf;
+  // lanes past the chunk read block gblk0 (always valid) and zero it, so the
+  // loads carry no branch and can all be in flight together
+  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * D + 8 * hf;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  constexpr int KH = D / 32;  // k-steps per half (loads of a half in flight together)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      x0 = *reinterpret_cast<const f32x4*>(kp + 16 * ks);
-      x1 = *reinterpret_cast<const f32x4*>(kp + 16 * ks + 4);
-    }
+  for (int half = 0; half < 2; ++half) {
+  f32x4 xa[KH], xb[KH];
+#pragma unroll
+  for (int kk = 0; kk < KH; ++kk) {
+    xa[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * (half * KH + kk));
+    xb[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * (half * KH + kk) + 4);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KH; ++kk) {
+    const int ks = half * KH + kk;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 x0 = ok ? xa[kk] : zero, x1 = ok ? xb[kk] : zero;
     bf16x8 hi, mid, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -166,6 +178,7 @@ __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qfrag[ks], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qfrag[ks], acc, 0, 0, 0);
   }
+  }
   // acc[r] = score of block 32 bt + 8 (r / 4) + 4 hf + (r % 4) for token 32 tt + (lane & 31)
 #pragma unroll
   for (int r = 0; r < 16; ++r)
@@ -177,8 +190,8 @@ template <int D>
 __device__ __forceinline__ void gate_scores_valu(const float (*qs)[D + 4], float (*ks)[D + 4],
                                                  const float* __restrict__ kbar, int H, int h,
                                                  int gblk0, int nb, int total_blocks,
-                                                 float (*ss)[kGateSpan + 1], int col0, int tid) {
-  for (int i = tid; i < kGateChunk * (D / 4); i += kGateWaves * 64) {
+                                                 float (*ss)[kGateStride], int col0, int tid) {
+  for (int i = tid; i < kGateChunkValu * (D / 4); i += kGateWaves * 64) {
     const int j = i / (D / 4), e4 = i % (D / 4);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (j < nb && gblk0 + j < total_blocks)
@@ -223,13 +236,13 @@ __device__ __forceinline__ void gate_scores_valu(const float (*qs)[D + 4], float
 // 32-bit order keys with ballot counts; among keys equal to the threshold the
 // lower block indices win.
 template <typename T, int D>
-__global__ __launch_bounds__(512) void gate_topk_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_topk_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
     int total_tokens, int total_blocks, int tiles_per_seq, int H, int block_size, int topk,
     int32_t* __restrict__ block_idx) {
   constexpr bool kMfma = sizeof(T) == 2;
-  __shared__ float ss[kGateRows][kGateSpan + 1];
+  __shared__ float ss[kGateRows][kGateStride];
   __shared__ uint32_t skey[kGateWaves][64];
   __shared__ int32_t sidx[kGateWaves][64];
 
@@ -258,8 +271,8 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
     // query operands: bf16 MFMA fragments in registers, or an fp32 LDS tile
     bf16x8 qfrag[D / 16];
     if constexpr (kMfma) {
-      const int tok = p0 + 32 * (w >> 1) + (lane & 31);
-      const bool qv = w < 4 && tok < len;
+      const int tok = p0 + 32 * (w >> 2) + (lane & 31);
+      const bool qv = tok < len;
       const uint16_t* qp = (const uint16_t*)q + ((size_t)(start + (qv ? tok : p0)) * H + h) * D +
                            8 * (lane >> 5);
 #pragma unroll
@@ -278,7 +291,7 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
         __syncthreads();
       } else {
         __shared__ __attribute__((aligned(16))) float qs[kGateRows][D + 4];
-        __shared__ __attribute__((aligned(16))) float ks[kGateChunk][D + 4];
+        __shared__ __attribute__((aligned(16))) float ks[kGateChunkValu][D + 4];
         if (base == 0) {
           for (int i = tid; i < kGateRows * (D / 4); i += kGateWaves * 64) {
             const int r = i / (D / 4), e4 = i % (D / 4);
@@ -288,9 +301,9 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
             *reinterpret_cast<f32x4*>(&qs[r][e4 * 4]) = v;
           }
         }
-        for (int cb = 0; cb < nspan; cb += kGateChunk)
-          gate_scores_valu<D>(qs, ks, kbar, H, h, gb0 + base + cb, min(kGateChunk, nspan - cb),
-                              total_blocks, ss, cb, tid);
+        for (int cb = 0; cb < nspan; cb += kGateChunkValu)
+          gate_scores_valu<D>(qs, ks, kbar, H, h, gb0 + base + cb,
+                              min(kGateChunkValu, nspan - cb), total_blocks, ss, cb, tid);
       }
 
       // The wave's 8 rows go through the radix select in lockstep (independent
@@ -298,6 +311,66 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
       // marks "no candidate" (lanes past the span, rows past the tile end,
       // unused slots of the kept set) and never reaches a threshold >= 1.
       constexpr int R = kGateRowsPerWave;
+      uint32_t prefix[R];
+      if (k1 <= kGateFastK) {
+        // Threshold = the k1-th largest key of the row, found with VALU work
+        // only: lane (row lane / 8, part lane % 8) keeps the sorted
+        // (descending) top 16 of the row's keys j = part, part + 8, ...
+        // (branch-free max/min insertion), the 8 parts are merged in three
+        // xor-shuffle rounds (the half-cleaner max(a_i, b_15-i) keeps the top
+        // 16 of both lists as a bitonic sequence, which a bitonic merge sorts).
+        const int rr = lane >> 3, part = lane & 7;
+        const int r = w * R + rr;
+        uint32_t top[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) top[i] = 0u;
+        auto insert = [&](uint32_t x) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t hi = max(top[i], x);
+            x = min(top[i], x);
+            top[i] = hi;
+          }
+        };
+        if (r < nq)
+          for (int j = part; j < nspan; j += 8) insert(order_key(ss[r][j]));
+        if (base > 0) {
+          // the row's kept set (at most k1 <= 16 keys, lanes 0..15 of the
+          // row-per-wave layout)
+          uint32_t a0 = 0u, a1 = 0u;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const uint32_t b0 = __shfl(tkey[i], part), b1 = __shfl(tkey[i], part + 8);
+            if (rr == i) { a0 = b0; a1 = b1; }
+          }
+          insert(a0);
+          insert(a1);
+        }
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+          uint32_t pt[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pt[i] = __shfl_xor(top[i], d);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) top[i] = max(top[i], pt[15 - i]);
+#pragma unroll
+          for (int dist = 8; dist >= 1; dist >>= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((i & dist) == 0) {
+                const uint32_t hi = max(top[i], top[i + dist]);
+                const uint32_t lo = min(top[i], top[i + dist]);
+                top[i] = hi;
+                top[i + dist] = lo;
+              }
+        }
+        // 0 when the row has fewer than k1 candidates: all of them are kept
+        uint32_t t = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t = (i == k1 - 1) ? top[i] : t;
+#pragma unroll
+        for (int i = 0; i < R; ++i) prefix[i] = __builtin_amdgcn_readlane(t, 8 * i);
+      }
       uint32_t nkey[R][4];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -306,18 +379,43 @@ __global__ __launch_bounds__(512) void gate_topk_kernel(
         for (int j = 0; j < 4; ++j)
           nkey[i][j] = (r < nq && lane + 64 * j < nspan) ? order_key(ss[r][lane + 64 * j]) : 0u;
       }
-      uint32_t prefix[R];
+      if (k1 > kGateFastK) {
+      // Bitwise radix select of the k1-th largest key, most significant bit
+      // first.  A row is settled as soon as exactly k1 keys reach the
+      // candidate prefix (they are the selection, whatever the lower bits),
+      // or from the start when it has at most k1 candidates (prefix 0 keeps
+      // them all).  Groups of 64 past the span and an empty kept set hold
+      // only key 0 and are not counted.
+      const int ngrp = (nspan + 63) / 64;
+      bool done[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) prefix[i] = 0u;
+      for (int i = 0; i < R; ++i) {
+        prefix[i] = 0u;
+        int total = tcnt[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < ngrp) total += (int)__popcll(__ballot(nkey[i][j] != 0u));
+        done[i] = total <= k1;
+      }
       for (int b = 31; b >= 0; --b) {
+        bool all = true;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          const uint32_t cand = prefix[i] | (1u << b);
-          int cnt = (int)__popcll(__ballot(tkey[i] >= cand));
+          if (!done[i]) {
+            const uint32_t cand = prefix[i] | (1u << b);
+            int cnt = tcnt[i] > 0 ? (int)__popcll(__ballot(tkey[i] >= cand)) : 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cnt += (int)__popcll(__ballot(nkey[i][j] >= cand));
-          if (cnt >= k1) prefix[i] = cand;
+            for (int j = 0; j < 4; ++j)
+              if (j < ngrp) cnt += (int)__popcll(__ballot(nkey[i][j] >= cand));
+            if (cnt >= k1) {
+              prefix[i] = cand;
+              done[i] = cnt == k1;
+            }
+          }
+          all = all && done[i];
         }
+        if (all) break;
+      }
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {

@@ -80,6 +80,24 @@ def test_gate_topk_32k_fine_grained(dev):
     print("32k", st)
 
 
+@pytest.mark.parametrize("w", [
+    # more than 256 past blocks: the selection runs over two spans and merges
+    # the first span's kept set; k - 1 = 4 (sorted-list threshold) and 20
+    # (radix threshold); ragged second sequence, d 64 and 128
+    inputs.custom([300 * 64 + 5, 700], 2, 128, 64, 5, "bf16", name="gate-2span-k5"),
+    inputs.custom([290 * 64], 2, 64, 64, 21, "bf16", name="gate-2span-k21"),
+    # k - 1 = 16: the largest k of the sorted-list threshold
+    inputs.custom([64 * 40 + 17], 3, 128, 64, 17, "bf16", name="gate-k17"),
+], ids=lambda w: w.name)
+def test_gate_topk_spans(dev, w):
+    _say("gate", w.name)
+    x = inputs.make_inputs(w, device=dev, seed=5)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    idx = moba.moba_gate_topk(x["q"], moba.moba_pool_keys(x["k"], geom), geom, w.topk)
+    st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx)
+    print(w.name, st)
+
+
 # ---------------------------------------------------------------------------
 # the whole forward
 # ---------------------------------------------------------------------------
