@@ -311,6 +311,92 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
       // marks "no candidate" (lanes past the span, rows past the tile end,
       // unused slots of the kept set) and never reaches a threshold >= 1.
       constexpr int R = kGateRowsPerWave;
+      if (c <= kGateSpan && k1 <= kGateFastK) {
+        // Single span, k1 <= 16: the whole selection in the 8-lanes-per-row
+        // layout, VALU only.  Lane (row lane / 8, part lane % 8) owns the
+        // candidates j = 32 part + m, m < 32 (its 32-bit word of the row's
+        // bitmap); the threshold is the k1-th largest key (sorted per-lane
+        // top 16, bitonic merges); the selection is every key above it plus
+        // the lowest-index keys equal to it, written in ascending order.
+        const int rr = lane >> 3, part = lane & 7;
+        const int r = w * R + rr;
+        const bool rv = r < nq;
+        auto key_at = [&](int m) {
+          const int j = 32 * part + m;
+          return (rv && j < nspan) ? order_key(ss[r][j]) : 0u;
+        };
+        uint32_t top[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) top[i] = 0u;
+        const int nm = min(32, nspan);
+        for (int mm = 0; mm < nm; ++mm) {
+          uint32_t x = key_at((mm + part) & 31);  // skewed: the 8 parts hit distinct banks
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t hi = max(top[i], x);
+            x = min(top[i], x);
+            top[i] = hi;
+          }
+        }
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+          uint32_t pt[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pt[i] = __shfl_xor(top[i], d);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) top[i] = max(top[i], pt[15 - i]);
+#pragma unroll
+          for (int dist = 8; dist >= 1; dist >>= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((i & dist) == 0) {
+                const uint32_t hi = max(top[i], top[i + dist]);
+                const uint32_t lo = min(top[i], top[i + dist]);
+                top[i] = hi;
+                top[i + dist] = lo;
+              }
+        }
+        uint32_t t = 0u;  // 0: fewer than k1 candidates, all of them are kept
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t = (i == k1 - 1) ? top[i] : t;
+        uint32_t gt = 0u, eq = 0u;
+        for (int mm = 0; mm < nm; ++mm) {
+          const int m = (mm + part) & 31;
+          const uint32_t x = key_at(m);
+          gt |= (uint32_t)(x > t && x != 0u) << m;
+          eq |= (uint32_t)(t != 0u && x == t) << m;
+        }
+        // sums and exclusive prefixes over the 8 parts of a row
+        auto row_scan = [&](int v, int& excl) {
+          int inc = v;
+#pragma unroll
+          for (int d = 1; d < 8; d <<= 1) {
+            const int u = __shfl_up(inc, d, 8);
+            if (part >= d) inc += u;
+          }
+          excl = inc - v;
+          return __shfl(inc, 7, 8);
+        };
+        int gt_before, eq_before, sel_before;
+        const int ngt = row_scan(__popc(gt), gt_before);
+        row_scan(__popc(eq), eq_before);
+        // keys equal to the threshold: lowest block indices first
+        int take = min(max(k1 - ngt - eq_before, 0), __popc(eq));
+        uint32_t sel = gt, e = eq;
+        for (; take > 0; --take) {
+          sel |= e & (~e + 1u);
+          e &= e - 1u;
+        }
+        const int nsel = row_scan(__popc(sel), sel_before);
+        if (rv) {
+          int32_t* out = block_idx + ((size_t)(start + p0 + r) * H + h) * topk;
+          int pos = sel_before;
+          for (uint32_t sm = sel; sm != 0u; sm &= sm - 1u)
+            out[pos++] = base + 32 * part + __builtin_ctz(sm);
+          for (int q = nsel + part; q < topk; q += 8) out[q] = q == nsel ? c : -1;
+        }
+        return;
+      }
       uint32_t prefix[R];
       if (k1 <= kGateFastK) {
         // Threshold = the k1-th largest key of the row, found with VALU work
