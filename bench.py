@@ -136,6 +136,78 @@ def cpu_baseline(x, w, rows_target, seconds):
     }
 
 
+def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False):
+    """Times `steps` MoBA layers (pool, gate + top-k, attention) on one
+    workload after `warmup` untimed ones, then the library's own dense causal
+    kernel `dense_reps` times.  Returns the inputs (if keep), the geometry,
+    ms per step, per-stage HIP-event totals, dense ms and dense stages."""
+    print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} d{w.head_dim} B{w.block_size} "
+          f"k{w.topk}", file=sys.stderr, flush=True)
+    x = inputs.make_inputs(w, device=dev)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    H, d = w.heads, w.head_dim
+    dt = moba.MOBA_BF16 if w.dtype == "bf16" else moba.MOBA_F32
+    kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((geom.total_tokens, H, w.topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(moba.moba_attn_workspace_bytes(dt, geom.total_tokens, geom.total_blocks,
+                                                    H, d, w.block_size, w.topk),
+                     dtype=torch.uint8, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+
+    def step():
+        moba.moba_pool_keys(k, geom, kbar=kbar)
+        moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+        moba.moba_attn_fwd(q, k, v, geom, w.topk, idx, w.scale, out=out, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    prof = moba.Profiler().attach()
+    prof.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    kern = prof.summary()
+    prof.reset()
+    print(f"[bench] {w.name}: moba {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # the library's own dense causal kernel on the same inputs
+    del ws
+    dense_ms = None
+    rec_dense_stages = {}
+    if dense_reps > 0:
+        dws = torch.empty(moba.moba_dense_workspace_bytes(dt, geom.total_tokens,
+                                                          geom.total_blocks, H, d, w.block_size),
+                          dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(q)
+        dlse = torch.empty_like(lse)
+        moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        prof.reset()
+        t0 = time.perf_counter()
+        for _ in range(dense_reps):
+            moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / dense_reps
+        rec_dense_stages = prof.summary()
+        del dout, dws
+        print(f"[bench] {w.name}: dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
+    prof.detach()
+    prof.close()
+    del kbar, idx, out, lse
+    if not keep:
+        del x, q, k, v
+        x = None
+        torch.cuda.empty_cache()
+    return x, geom, ms_step, kern, dense_ms, rec_dense_stages
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +218,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--also", default="32k",
+                    help="comma-separated extra workloads reported under other_workloads "
+                         "(ms/layer, TFLOP/s, dense, speedup); empty for none")
+    ap.add_argument("--also-steps", type=int, default=20)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -171,68 +247,12 @@ def main():
         print(json.dumps({"copy_probe_bytes": 4 * n, "launches": 3}))
         return
 
-    w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} d{w.head_dim} B{w.block_size} "
-          f"k{w.topk}", file=sys.stderr, flush=True)
-    x = inputs.make_inputs(w, device=dev)
-    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    w = inputs.WORKLOADS[args.workload]
+    x, geom, ms_step, kern, dense_ms, rec_dense_stages = measure(
+        torch, inputs, moba, w, dev, args.steps, args.warmup, args.dense_reps, keep=True)
     H, d = w.heads, w.head_dim
-    dt = moba.MOBA_BF16 if w.dtype == "bf16" else moba.MOBA_F32
-    kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=dev)
-    idx = torch.empty((geom.total_tokens, H, w.topk), dtype=torch.int32, device=dev)
-    out = torch.empty_like(x["q"])
-    lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(moba.moba_attn_workspace_bytes(dt, geom.total_tokens, geom.total_blocks,
-                                                    H, d, w.block_size, w.topk),
-                     dtype=torch.uint8, device=dev)
-    q, k, v = x["q"], x["k"], x["v"]
-
-    def step():
-        moba.moba_pool_keys(k, geom, kbar=kbar)
-        moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
-        moba.moba_attn_fwd(q, k, v, geom, w.topk, idx, w.scale, out=out, lse=lse, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    prof = moba.Profiler().attach()
-    prof.reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern = prof.summary()
-    prof.reset()
-    print(f"[bench] moba {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-
-    # the library's own dense causal kernel on the same inputs
-    del ws
-    dense_ms = None
-    rec_dense_stages = {}
-    if args.dense_reps > 0:
-        dws = torch.empty(moba.moba_dense_workspace_bytes(dt, geom.total_tokens,
-                                                          geom.total_blocks, H, d, w.block_size),
-                          dtype=torch.uint8, device=dev)
-        dout = torch.empty_like(q)
-        dlse = torch.empty_like(lse)
-        moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
-        torch.cuda.synchronize()
-        prof.reset()
-        t0 = time.perf_counter()
-        for _ in range(args.dense_reps):
-            moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
-        torch.cuda.synchronize()
-        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_reps
-        rec_dense_stages = prof.summary()
-        del dout, dws
-        print(f"[bench] dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
-    prof.detach()
-    prof.close()
-
+    q = x["q"]
     pairs, hist_p, own_p = attended_pairs(w.seqlens, w.block_size, w.topk, H)
     flops = 4.0 * d * pairs
     eff_tflops = flops / (ms_step * 1e-3) / 1e12
@@ -287,6 +307,24 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_rows, args.cpu_seconds)
+    del x, q
+    torch.cuda.empty_cache()
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != w.name]:
+        wo = inputs.WORKLOADS[name]
+        _, _, ms_o2, kern_o, dense_o, _ = measure(torch, inputs, moba, wo, dev, args.also_steps,
+                                                  max(1, args.warmup), 2 if args.dense_reps else 0)
+        pairs_o, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
+        others[name] = {
+            "config": {"seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": wo.head_dim,
+                       "block_size": wo.block_size, "topk": wo.topk},
+            "ms_per_layer": ms_o2,
+            "effective_tflops": 4.0 * wo.head_dim * pairs_o / (ms_o2 * 1e-3) / 1e12,
+            "dense_ms": dense_o,
+            "speedup_vs_dense": (dense_o / ms_o2) if dense_o else None,
+            "stages_ms": {n: t / args.also_steps for n, (c, t) in kern_o.items()},
+        }
+    rec["other_workloads"] = others
     print(json.dumps(rec), flush=True)
 
 
