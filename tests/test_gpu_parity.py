@@ -137,12 +137,34 @@ def test_moba_sampled(dev, name, per_head, heads):
 
 
 def test_moba_1m_sampled(dev):
+    """The 1M-token workload in the launch configuration bench.py times:
+    outputs on 512 seeded rows (4 heads), selections on every row of one
+    head, and causal validity of every selection row."""
     w = inputs.WORKLOADS["1m"]
     x, geom, out, lse, idx = _run(w, dev)
-    rows = inputs.sample_rows(w, 48, heads=[3, 28])
+    rows = inputs.sample_rows(w, 128, heads=[0, 3, 17, 28])
     st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
                                 w.scale, out, lse, idx, rows, parity.BF16_TOL)
     print("1m", st)
+    st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx,
+                                   heads=[5])
+    print("1m head 5 selections", st)
+    # every row: ascending past blocks, then the own block, then -1 padding,
+    # min(k, c + 1) entries
+    T, H, k = idx.shape
+    c = (torch.arange(T, device=idx.device) // w.block_size).view(T, 1, 1)
+    valid = idx >= 0
+    n = valid.sum(-1, keepdim=True)
+    assert torch.equal(n, torch.clamp(c, max=k - 1).expand(T, H, 1) + 1)
+    pos = torch.arange(k, device=idx.device).view(1, 1, k)
+    assert bool((valid == (pos < n)).all())
+    own = torch.gather(idx, 2, n - 1)
+    assert torch.equal(own, c.expand(T, H, 1))
+    past = torch.where(pos < n - 1, idx, torch.full_like(idx, -1))
+    assert bool(((past < c) | (past == -1)).all())
+    inc = past[..., 1:] > past[..., :-1]
+    assert bool((inc | (past[..., 1:] == -1)).all())
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
 
 
 # ---------------------------------------------------------------------------
