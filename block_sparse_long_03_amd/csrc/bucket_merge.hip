@@ -13,85 +13,105 @@
 
 namespace moba {
 
-constexpr int kBucketTokens = 2048;   // tokens per workgroup in count/scatter
-constexpr int kBucketLdsBins = 4096;  // LDS histogram limit (past blocks per tile)
+constexpr int kBucketTokensMax = 256;  // tokens per workgroup in count/scatter (all heads)
+constexpr int kBucketLdsBins = 8192;  // LDS histogram limit (heads x past blocks per tile)
 
-// Per (sequence tile, head): histogram of the historical selections in LDS,
-// flushed with one global atomic per touched block.
+// Per (sequence tile of `tile_tokens` tokens): every (token, head) row of
+// block_idx, read in memory order (consecutive lanes take consecutive rows,
+// so a wave reads one contiguous range), counted into an LDS histogram per
+// (head, past block) and flushed with one global atomic per touched bin.
+// The scatter pass reserves a range per bin, then places each entry.
 template <bool kScatter>
 __global__ __launch_bounds__(256) void bucket_pass_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int H,
-    int NB, int block_size, int topk, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int tile_tokens,
+    int H, int NB, int block_size, int topk, int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ list) {
   __shared__ int32_t hist[kBucketLdsBins];
   __shared__ int32_t basev[kScatter ? kBucketLdsBins : 1];
   const int sid = blockIdx.x / tiles_per_seq;
   const int tile = blockIdx.x % tiles_per_seq;
-  const int h = blockIdx.y;
   int start, len;
   seq_span(cu_seqlens, sid, total_tokens, &start, &len);
-  const int p0 = tile * kBucketTokens;
+  const int p0 = tile * tile_tokens;
   if (p0 >= len) return;
-  const int p1 = min(len, p0 + kBucketTokens);
+  const int p1 = min(len, p0 + tile_tokens);
   const int nbins = (p1 - 1) / block_size;  // past blocks of the last row
   const int gb0 = cu_blocks[sid];
-  const bool use_lds = nbins <= kBucketLdsBins;
-  int32_t* keyrow = counts + (size_t)h * NB + gb0;
+  const bool use_lds = nbins * H <= kBucketLdsBins;
+  const int nrows = (p1 - p0) * H;
+  const int32_t* rows = block_idx + ((size_t)(start + p0) * H) * topk;
 
   if (use_lds) {
-    for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0;
+    for (int b = threadIdx.x; b < nbins * H; b += 256) hist[b] = 0;
     __syncthreads();
   }
-  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
+  // walks row r = (p - p0) * H + h, calling f(h, e, slot) for each accepted
+  // historical entry (0 <= e < c, increasing, inside the batch's blocks)
+  auto walk = [&](int r, auto&& f) {
+    const int p = p0 + r / H;
+    const int h = r - (r / H) * H;
     const int c = p / block_size;
-    const int32_t* row = block_idx + ((size_t)(start + p) * H + h) * topk;
+    const int32_t* row = rows + (size_t)r * topk;
     int last = -1, nh = 0;
-    for (int j = 0; j < topk; ++j) {
-      const int e = row[j];
+    auto visit = [&](int e) {
       if (e >= 0 && e < c && e > last) {
         last = e;
-        if (gb0 + e >= NB) { ++nh; continue; }  // inconsistent geometry: drop
-        if (!kScatter) {
-          if (use_lds) atomicAdd(&hist[e], 1); else atomicAdd(&keyrow[e], 1);
-        } else if (!use_lds) {
-          const int pos = offsets[(size_t)h * NB + gb0 + e] + atomicAdd(&keyrow[e], 1);
-          list[pos] = (start + p) * topk + nh;
-        } else {
-          atomicAdd(&hist[e], 1);
-        }
+        if (gb0 + e < NB) f(h, e, nh, p);  // else inconsistent geometry: dropped
         ++nh;
       }
+    };
+    if ((topk & 3) == 0) {  // rows are 16-byte aligned: whole int4 loads
+      for (int j = 0; j < topk; j += 4) {
+        const int4 e4 = *reinterpret_cast<const int4*>(row + j);
+        visit(e4.x);
+        visit(e4.y);
+        visit(e4.z);
+        visit(e4.w);
+      }
+    } else {
+      for (int j = 0; j < topk; ++j) visit(row[j]);
     }
-  }
-  if (!use_lds) return;
-  __syncthreads();
+  };
   if (!kScatter) {
-    for (int b = threadIdx.x; b < nbins; b += 256)
-      if (hist[b] && gb0 + b < NB) atomicAdd(&keyrow[b], hist[b]);
+    for (int r = threadIdx.x; r < nrows; r += 256)
+      walk(r, [&](int h, int e, int, int) {
+        if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
+        else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
+      });
+    if (!use_lds) return;
+    __syncthreads();
+    for (int b = threadIdx.x; b < nbins * H; b += 256) {
+      const int h = b / nbins, e = b - (b / nbins) * nbins;
+      if (hist[b]) atomicAdd(&counts[(size_t)h * NB + gb0 + e], hist[b]);
+    }
     return;
   }
-  // scatter: reserve a range per touched block, then place every entry
-  for (int b = threadIdx.x; b < nbins; b += 256) {
+  if (!use_lds) {
+    for (int r = threadIdx.x; r < nrows; r += 256)
+      walk(r, [&](int h, int e, int slot, int p) {
+        const size_t key = (size_t)h * NB + gb0 + e;
+        list[offsets[key] + atomicAdd(&counts[key], 1)] = (start + p) * topk + slot;
+      });
+    return;
+  }
+  for (int r = threadIdx.x; r < nrows; r += 256)
+    walk(r, [&](int h, int e, int, int) { atomicAdd(&hist[h * nbins + e], 1); });
+  __syncthreads();
+  // reserve a range per touched bin, then place every entry
+  for (int b = threadIdx.x; b < nbins * H; b += 256) {
+    const int h = b / nbins, e = b - (b / nbins) * nbins;
     const int n = hist[b];
-    basev[b] = n && gb0 + b < NB ? offsets[(size_t)h * NB + gb0 + b] + atomicAdd(&keyrow[b], n) : 0;
+    const size_t key = (size_t)h * NB + gb0 + e;
+    basev[b] = n ? offsets[key] + atomicAdd(&counts[key], n) : 0;
     hist[b] = 0;
   }
   __syncthreads();
-  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
-    const int c = p / block_size;
-    const int32_t* row = block_idx + ((size_t)(start + p) * H + h) * topk;
-    int last = -1, nh = 0;
-    for (int j = 0; j < topk; ++j) {
-      const int e = row[j];
-      if (e >= 0 && e < c && e > last) {
-        last = e;
-        if (gb0 + e >= NB) { ++nh; continue; }
-        list[basev[e] + atomicAdd(&hist[e], 1)] = (start + p) * topk + nh;
-        ++nh;
-      }
-    }
-  }
+  for (int r = threadIdx.x; r < nrows; r += 256)
+    walk(r, [&](int h, int e, int slot, int p) {
+      const int b = h * nbins + e;
+      list[basev[b] + atomicAdd(&hist[b], 1)] = (start + p) * topk + slot;
+    });
 }
 
 // Exclusive scans of the per-(head, block) counts (entries and tiles of
@@ -161,17 +181,20 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
     hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
                        counts, n);
   }
-  const int tiles = (g.max_seqlen + kBucketTokens - 1) / kBucketTokens;
-  dim3 grid(g.num_seqs * tiles, g.num_heads);
+  // tiles of 32..256 tokens, small enough for about 1024 workgroups
+  int tile_tokens = kBucketTokensMax;
+  while (tile_tokens > 32 && (long long)g.total_tokens < 1024LL * tile_tokens) tile_tokens >>= 1;
+  const int tiles = (g.max_seqlen + tile_tokens - 1) / tile_tokens;
+  dim3 grid(g.num_seqs * tiles);
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<false>), grid, dim3(256), 0, st, block_idx,
-                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, g.num_heads,
+                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
                        g.total_blocks, g.block_size, topk, counts, offsets, list);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, st, counts, n, tile_q,
                      offsets, tile_offsets);
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<true>), grid, dim3(256), 0, st, block_idx,
-                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, g.num_heads,
+                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
                        g.total_blocks, g.block_size, topk, counts, offsets, list);
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
