@@ -111,13 +111,13 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-constexpr int kGateRows = 64;    // query tokens per workgroup (they share one own block c)
+constexpr int kGateRows = 32;    // query tokens per workgroup (they share one own block c)
 constexpr int kGateSpan = 256;   // past blocks per selection pass (4 per lane)
 constexpr int kGateStride = kGateSpan + 8;  // LDS row stride of the scores (8 banks apart)
 constexpr int kGateFastK = 16;   // k - 1 up to this: threshold from sorted per-lane lists
 constexpr int kGateChunk = 128;  // past blocks per MFMA scoring step (one 32 x 32 tile per wave)
 constexpr int kGateChunkValu = 64;  // past blocks per fp32 scoring step
-constexpr int kGateWaves = 8;
+constexpr int kGateWaves = 4;
 constexpr int kGateRowsPerWave = kGateRows / kGateWaves;
 
 // exact split of an fp32 value into three bf16 parts: x = hi + mid + lo
@@ -130,11 +130,11 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r1 - m);  // at most 8 significant bits remain: exact
 }
 
-// Scores of a chunk of up to 128 past blocks for the 64 query rows, written
+// Scores of a chunk of up to 128 past blocks for the 32 query rows, written
 // to ss[row][col0 + j].  bf16 queries: s = q . kbar with kbar split exactly
 // into three bf16 parts and the three products summed by
 // v_mfma_f32_32x32x16_bf16 (products exact, fp32 accumulation); each of the
-// 8 waves owns one 32 x 32 tile (token tile w / 4, block tile w % 4).
+// 4 waves owns one 32 x 32 tile (block tile w).
 template <int D>
 __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
                                                  const float* __restrict__ kbar, int H, int h,
@@ -228,15 +228,14 @@ __device__ __forceinline__ void gate_scores_valu(const float (*qs)[D + 4], float
   __syncthreads();  // ks is reused by the next chunk
 }
 
-// One workgroup handles 64 consecutive query tokens of one sequence and head
-// (B is a multiple of 64, so they share their own block c).  The past blocks
-// are scored into LDS up to 256 at a time; then each wave merges, for each of
-// its 8 rows, those candidates into the running top-(k-1) set held in lanes
-// 0..k-2 (ascending block index).  The merge is an exact radix select over
-// 32-bit order keys with ballot counts; among keys equal to the threshold the
-// lower block indices win.
+// One workgroup (4 waves, small enough for four per CU) handles 32
+// consecutive query tokens of one sequence and head (B is a multiple of 64,
+// so they share their own block c).  The past blocks are scored into LDS up
+// to 256 at a time; each wave then selects for its 8 rows (see the two
+// selection paths below); among keys equal to the threshold the lower block
+// indices win.
 template <typename T, int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_topk_kernel(
+__global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void gate_topk_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
     int total_tokens, int total_blocks, int tiles_per_seq, int H, int block_size, int topk,
