@@ -312,11 +312,12 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
       constexpr int R = kGateRowsPerWave;
       if (c <= kGateSpan && k1 <= kGateFastK) {
         // Single span, k1 <= 16: the whole selection in the 8-lanes-per-row
-        // layout, VALU only.  Lane (row lane / 8, part lane % 8) owns the
-        // candidates j = 32 part + m, m < 32 (its 32-bit word of the row's
-        // bitmap); the threshold is the k1-th largest key (sorted per-lane
-        // top 16, bitonic merges); the selection is every key above it plus
-        // the lowest-index keys equal to it, written in ascending order.
+        // layout, VALU only.  The threshold is the k1-th largest key (sorted
+        // per-lane top 16, bitonic merges); lane (row lane / 8, part
+        // lane % 8) then owns the candidates j = 32 part + m, m < 32 (its
+        // 32-bit word of the row's bitmap): the selection is every key above
+        // the threshold plus the lowest-index keys equal to it, written in
+        // ascending order.
         const int rr = lane >> 3, part = lane & 7;
         const int r = w * R + rr;
         const bool rv = r < nq;
@@ -327,9 +328,11 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
         uint32_t top[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) top[i] = 0u;
-        const int nm = min(32, nspan);
-        for (int mm = 0; mm < nm; ++mm) {
-          uint32_t x = key_at((mm + part) & 31);  // skewed: the 8 parts hit distinct banks
+        // the threshold pass takes the row's keys strided (j = part + 8 m),
+        // so each lane inserts only ceil(nspan / 8) of them; the 8 parts of a
+        // row sit in distinct banks (row stride 8 banks)
+        for (int j = part; j < nspan; j += 8) {
+          uint32_t x = rv ? order_key(ss[r][j]) : 0u;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const uint32_t hi = max(top[i], x);
@@ -337,6 +340,7 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
             top[i] = hi;
           }
         }
+        const int nm = min(32, nspan);
 #pragma unroll
         for (int d = 1; d < 8; d <<= 1) {
           uint32_t pt[16];
