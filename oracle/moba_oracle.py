@@ -37,7 +37,8 @@ Blockwise attention followed by an online-softmax merge reaches exactly this
 softmax over J (the merge is an exact identity), so the oracle computes the
 softmax over J directly and never merges.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against hand
+Every function here is pinned by ``tests/test_oracle_pins.py`` (the static
+routing rules by ``tests/test_static_gate_pins.py``) against hand
 worked examples, library routines (torch SDPA in fp64 for the k >= n and k = 1
 reductions), closed forms and invariants.  The pages print no numeric output
 of the operator itself; the only printed numbers this oracle reproduces are
@@ -327,6 +328,79 @@ def selection_is_valid(Q, K, cu_seqlens, block_size, topk, row, idx_row,
         return True
     best_out = max(others)
     return bool(best_out - worst_in <= rel * max(abs(best_out), abs(worst_in)))
+
+
+# --------------------------------------------------------------------------
+# static gates: fixed routing rules run through the same attention
+# --------------------------------------------------------------------------
+
+def static_select_row(c, topk, sink):
+    """Static routing for a query whose own block is c.
+
+    [wispaper] "Why the Change Is Plausible" (first paragraph) and
+    [cn-summary] 与其他方法的关系: sliding-window attention is a gate that
+    always picks the most recent blocks, attention-sink attention one that
+    always picks the initial blocks plus the recent ones, and full attention
+    the degenerate gate with k = n.  Read here as one rule with the same
+    causality as the learned gate (own block always taken and counted in k,
+    never a future block):
+
+    1. take the own block c;
+    2. take the initial blocks 0, 1, ... while fewer than ``sink`` of them are
+       taken, a past block is left and fewer than k blocks are taken;
+    3. walk back from c - 1 over the past blocks not yet taken, taking each
+       while fewer than k blocks are taken.
+
+    sink = 0 is a sliding window of k blocks; topk >= c + 1 takes every block
+    0..c (full causal attention).  Returns idx [topk] int64 ascending, -1
+    padded.
+    """
+    taken = [c]
+    i = 0
+    while i < sink and i < c and len(taken) < topk:
+        taken.append(i)
+        i += 1
+    j = c - 1
+    while j >= 0 and len(taken) < topk:
+        if j not in taken:
+            taken.append(j)
+        j -= 1
+    idx = np.full(topk, -1, dtype=np.int64)
+    chosen = sorted(taken)
+    idx[:len(chosen)] = chosen
+    return idx
+
+
+def static_reference(Q, K, V, cu_seqlens, block_size, topk, sink, scale, rows=None):
+    """Attention with the static routing of ``static_select_row`` on (token,
+    head) rows: steps 4-5 over the statically chosen blocks.  Returns dict with
+    rows, out [R, d], lse [R], idx [R, topk]."""
+    T, H, d = Q.shape
+    rows = _rows_by_head(rows, T, H)
+    R = len(rows)
+    out = np.zeros((R, d))
+    lse = np.zeros(R)
+    idx = np.full((R, topk), -1, dtype=np.int64)
+    for r, (t, h) in enumerate(rows):
+        s, a, L = _seq_of_token(cu_seqlens, int(t))
+        tl = int(t) - a
+        idx[r] = static_select_row(tl // block_size, topk, sink)
+        J = attended_tokens(idx[r], tl, block_size)
+        out[r], lse[r] = attend_row(Q[t, h, :], K[a:a + L, h, :], V[a:a + L, h, :], J, scale)
+    return dict(rows=rows, out=out, lse=lse, idx=idx)
+
+
+def static_select(cu_seqlens, block_size, topk, sink):
+    """``static_select_row`` for every token of a packed batch: idx [T, topk]
+    (the rule does not depend on the head)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    idx = np.full((T, topk), -1, dtype=np.int64)
+    for a, L in sequences(cu):
+        for c in range(num_blocks(L, block_size)):
+            row = static_select_row(c, topk, sink)
+            idx[a + c * block_size:a + min((c + 1) * block_size, L)] = row
+    return idx
 
 
 # --------------------------------------------------------------------------
