@@ -217,6 +217,28 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
+moba_status moba_static_select(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                               int num_seqs, int total_tokens, int max_seqlen, int total_blocks,
+                               int num_heads, int block_size, int topk, int sink_blocks,
+                               int32_t* block_idx, void* stream) {
+  // the selection does not depend on dtype or head_dim: any supported pair
+  // checks the rest of the geometry
+  moba_status st = check_geometry(MOBA_BF16, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, 64, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (sink_blocks < 0) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!block_idx) return MOBA_ERR_INVALID_ARG;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, 64, block_size);
+  hipError_t e = timed("static_select", (hipStream_t)stream, [&] {
+    return moba::launch_static_select(g, topk, sink_blocks, block_idx, (hipStream_t)stream);
+  });
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
 size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks, int num_heads,
                                  int head_dim, int block_size, int topk) {
   if (!dtype_ok(dtype) || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||

@@ -565,6 +565,38 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
 }
 
 // ---------------------------------------------------------------------------
+// static routing: fixed gates (sliding window, sink + window, full attention)
+// ---------------------------------------------------------------------------
+// Row of a query whose own block is c, as a closed form: with every block
+// taken when c < topk, else the s = min(sink, topk - 1) initial blocks and
+// the topk - s most recent blocks c - (topk - 1 - s) .. c, ascending.
+constexpr int kStaticTokens = 64;  // tokens per workgroup
+
+__global__ __launch_bounds__(256) void static_select_kernel(
+    const int32_t* __restrict__ cu_seqlens, int total_tokens, int tiles, int H, int block_size,
+    int topk, int sink, int32_t* __restrict__ block_idx) {
+  const int s = blockIdx.x / tiles;
+  const int p0 = (blockIdx.x - s * tiles) * kStaticTokens;
+  int start, len;
+  seq_span(cu_seqlens, s, total_tokens, &start, &len);
+  if (p0 >= len) return;
+  const int n = min(kStaticTokens, len - p0);
+  const int hk = H * topk;
+  const int sk = min(sink, topk - 1);
+  int32_t* out = block_idx + (size_t)(start + p0) * hk;
+  // consecutive threads write consecutive entries of the tile's rows
+  for (int e = threadIdx.x; e < n * hk; e += blockDim.x) {
+    const int tok = e / hk;
+    const int j = (e - tok * hk) % topk;
+    const int c = (p0 + tok) / block_size;
+    int v;
+    if (c < topk) v = j <= c ? j : -1;
+    else v = j < sk ? j : c - (topk - 1 - sk) + (j - sk);
+    out[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
 hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar,
@@ -600,6 +632,16 @@ hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const G
     if (g.head_dim == 128) MOBA_GATE(float, 128); else MOBA_GATE(float, 64);
   }
 #undef MOBA_GATE
+  return hipGetLastError();
+}
+
+hipError_t launch_static_select(const Geo& g, int topk, int sink, int32_t* block_idx,
+                                hipStream_t st) {
+  if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
+  const int tiles = (g.max_seqlen + kStaticTokens - 1) / kStaticTokens;
+  hipLaunchKernelGGL(static_select_kernel, dim3(g.num_seqs * tiles), dim3(256), 0, st,
+                     g.cu_seqlens, g.total_tokens, tiles, g.num_heads, g.block_size, topk, sink,
+                     block_idx);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ MOBA_F32 = 0
 MOBA_BF16 = 1
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
-           "moba_gate_topk", "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_gate_topk", "moba_static_select", "moba_attn_workspace_bytes", "moba_attn_fwd",
            "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
            "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
            "moba_profiler_names", "moba_profiler_destroy"]
@@ -66,6 +66,8 @@ def lib():
     L.moba_pool_keys.argtypes = [vp, i32] + geo + [vp, vp]
     L.moba_gate_topk.restype = i32
     L.moba_gate_topk.argtypes = [vp, i32, vp] + geo + [i32, vp, vp]
+    L.moba_static_select.restype = i32
+    L.moba_static_select.argtypes = [vp, vp] + [i32] * 8 + [vp, vp]
     L.moba_attn_workspace_bytes.restype = sz
     L.moba_attn_workspace_bytes.argtypes = [i32] * 7
     L.moba_attn_fwd.restype = i32
@@ -173,6 +175,21 @@ def moba_gate_topk(q, kbar, geom, topk, block_idx=None, stream=None):
     return block_idx
 
 
+def moba_static_select(geom, num_heads, topk, sink_blocks, block_idx=None, device=None,
+                       stream=None):
+    """Static routing rows (sliding window with sink_blocks = 0, sink + window
+    otherwise, full attention when topk covers every block) in the
+    moba_gate_topk format: block_idx [T, H, topk] int32."""
+    if block_idx is None:
+        block_idx = torch.empty((geom.total_tokens, num_heads, topk), dtype=torch.int32,
+                                device=device if device is not None else geom.cu_seqlens.device)
+    _check("moba_static_select", lib().moba_static_select(
+        _ptr(geom.cu_seqlens), _ptr(geom.cu_blocks), geom.num_seqs, geom.total_tokens,
+        geom.max_seqlen, geom.total_blocks, int(num_heads), geom.block_size, int(topk),
+        int(sink_blocks), _ptr(block_idx), _stream(stream)))
+    return block_idx
+
+
 def moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
                               block_size, topk):
     return int(lib().moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
@@ -272,6 +289,17 @@ def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=N
     Returns (out, lse, block_idx)."""
     kbar = moba_pool_keys(k, geom, stream=stream)
     idx = moba_gate_topk(q, kbar, geom, topk, stream=stream)
+    out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
+                             workspace=workspace, stream=stream)
+    return out, lse, idx
+
+
+def forward_static(q, k, v, geom, topk, sink_blocks, scale, out_dtype=None, workspace=None,
+                   stream=None):
+    """Attention through a static gate (sliding window / sink + window / full):
+    static routing -> sparse attention.  Returns (out, lse, block_idx)."""
+    H, d = _qkv_shape(q, geom)
+    idx = moba_static_select(geom, H, topk, sink_blocks, device=q.device, stream=stream)
     out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
                              workspace=workspace, stream=stream)
     return out, lse, idx

@@ -119,6 +119,29 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
                            void* stream);
 
 /*
+ * Static routing: a fixed gate in place of moba_gate_topk.
+ * "MoBA: Learned Block Sparsity for Long-Context Attention", section "Why
+ * the Change Is Plausible" (static sparse patterns as special cases of the
+ * gate: sliding-window attention always routes to the most recent blocks,
+ * attention-sink attention to the initial blocks plus the recent ones, full
+ * attention is k = n).  With the same causality as the learned gate, the row
+ * of a query whose own block is c holds
+ *   every block 0..c                                  when c < topk, else
+ *   blocks 0..s-1 and c-(topk-1-s)..c, s = min(sink_blocks, topk - 1),
+ * ascending, then -1 padding.  sink_blocks = 0 is a sliding window of topk
+ * blocks (own included); topk >= the longest sequence's block count is full
+ * causal attention.  The rows are the same for every head.
+ *   block_idx   [total_tokens, num_heads, topk] int32, written in full, in
+ *               the format of moba_gate_topk (input of moba_attn_fwd)
+ *   sink_blocks >= 0 (MOBA_ERR_INVALID_ARG otherwise)
+ * Geometry arguments as for the other calls (block_size a multiple of 64).
+ */
+moba_status moba_static_select(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                               int num_seqs, int total_tokens, int max_seqlen,
+                               int total_blocks, int num_heads, int block_size, int topk,
+                               int sink_blocks, int32_t* block_idx, void* stream);
+
+/*
  * Workspace bytes moba_attn_fwd needs for this geometry (0 when the
  * arguments are invalid).  The workspace holds the per-(KV block, head)
  * query lists, the per-(query, selected block) partial results and a

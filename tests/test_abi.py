@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
@@ -81,6 +81,24 @@ def test_invalid_arguments(L):
     assert attn(L, out_dtype=5) == E
     assert attn(L, ws=None) == E
     assert attn(L, ws=ctypes.c_void_p(0x10010)) == E   # not 256-byte aligned
+
+
+def static(L, topk=3, sink=1, idx=FAKE, **kw):
+    g = dict(GEO, **kw)
+    return L.moba_static_select(g["cu"], g["cb"], g["S"], g["T"], g["maxL"], g["NB"], g["H"],
+                                g["B"], topk, sink, idx, None)
+
+
+def test_static_select_arguments(L):
+    E, U = moba.MOBA_ERR_INVALID_ARG, moba.MOBA_ERR_UNSUPPORTED
+    assert static(L, sink=-1) == E
+    assert static(L, topk=0) == E
+    assert static(L, idx=None) == E
+    assert static(L, cu=None) == E
+    assert static(L, NB=7) == E
+    assert static(L, topk=65) == U
+    assert static(L, B=96) == U
+    assert static(L, T=0, maxL=0, NB=0, idx=None) == moba.MOBA_OK   # empty batch: nothing to do
 
 
 def test_unsupported(L):
