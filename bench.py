@@ -136,13 +136,16 @@ def cpu_baseline(x, w, rows_target, seconds):
     }
 
 
-def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False):
+def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, sink=None):
     """Times `steps` MoBA layers (pool, gate + top-k, attention) on one
     workload after `warmup` untimed ones, then the library's own dense causal
-    kernel `dense_reps` times.  Returns the inputs (if keep), the geometry,
-    ms per step, per-stage HIP-event totals, dense ms and dense stages."""
+    kernel `dense_reps` times.  With `sink` set, the learned gate is replaced
+    by the static routing of moba_static_select (sink 0: sliding window).
+    Returns the inputs (if keep), the geometry, ms per step, per-stage
+    HIP-event totals, dense ms and dense stages."""
+    gate = "learned" if sink is None else f"static sink {sink}"
     print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} d{w.head_dim} B{w.block_size} "
-          f"k{w.topk}", file=sys.stderr, flush=True)
+          f"k{w.topk} gate {gate}", file=sys.stderr, flush=True)
     x = inputs.make_inputs(w, device=dev)
     geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
     H, d = w.heads, w.head_dim
@@ -157,8 +160,11 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False):
     q, k, v = x["q"], x["k"], x["v"]
 
     def step():
-        moba.moba_pool_keys(k, geom, kbar=kbar)
-        moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+        if sink is None:
+            moba.moba_pool_keys(k, geom, kbar=kbar)
+            moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+        else:
+            moba.moba_static_select(geom, H, w.topk, sink, block_idx=idx)
         moba.moba_attn_fwd(q, k, v, geom, w.topk, idx, w.scale, out=out, lse=lse, workspace=ws)
 
     for _ in range(warmup):
@@ -218,10 +224,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--also", default="32k",
+    ap.add_argument("--also", default="32k,1m:window,1m:sink1",
                     help="comma-separated extra workloads reported under other_workloads "
-                         "(ms/layer, TFLOP/s, dense, speedup); empty for none")
-    ap.add_argument("--also-steps", type=int, default=20)
+                         "(ms/layer, TFLOP/s, dense, speedup); NAME:window or NAME:sinkN "
+                         "replaces the learned gate by static routing; empty for none")
+    ap.add_argument("--also-steps", type=int, default=20,
+                    help="timed steps of the extra workloads (3 above 256K tokens)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -311,18 +319,37 @@ def main():
     torch.cuda.empty_cache()
     others = {}
     for name in [n for n in args.also.split(",") if n and n != w.name]:
-        wo = inputs.WORKLOADS[name]
-        _, _, ms_o2, kern_o, dense_o, _ = measure(torch, inputs, moba, wo, dev, args.also_steps,
-                                                  max(1, args.warmup), 2 if args.dense_reps else 0)
+        wname, _, gate = name.partition(":")
+        sink = None
+        if gate == "window":
+            sink = 0
+        elif gate.startswith("sink"):
+            sink = int(gate[4:])
+        elif gate:
+            raise SystemExit(f"unknown gate {gate!r} in --also")
+        wo = inputs.WORKLOADS[wname]
+        steps_o = args.also_steps if wo.total_tokens <= (1 << 18) else min(args.also_steps, 3)
+        # the dense time of a workload is measured once, with its learned-gate line
+        dense_reps_o = 2 if (args.dense_reps and sink is None) else 0
+        _, _, ms_o2, kern_o, dense_o, _ = measure(torch, inputs, moba, wo, dev, steps_o,
+                                                  max(1, args.warmup), dense_reps_o, sink=sink)
+        if dense_o is None and wname == w.name:
+            dense_o = dense_ms
         pairs_o, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
+        n_ho, ms_ho = kern_o.get("attn_hist", (0, 0.0))
+        hist_o = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)[1]
         others[name] = {
-            "config": {"seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": wo.head_dim,
+            "config": {"workload": wname, "gate": gate or "learned",
+                       "seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": wo.head_dim,
                        "block_size": wo.block_size, "topk": wo.topk},
+            "steps": steps_o,
+            "attn_hist_tflops": (4.0 * wo.head_dim * hist_o / (ms_ho / n_ho * 1e-3) / 1e12
+                                 if n_ho else None),
             "ms_per_layer": ms_o2,
             "effective_tflops": 4.0 * wo.head_dim * pairs_o / (ms_o2 * 1e-3) / 1e12,
             "dense_ms": dense_o,
             "speedup_vs_dense": (dense_o / ms_o2) if dense_o else None,
-            "stages_ms": {n: t / args.also_steps for n, (c, t) in kern_o.items()},
+            "stages_ms": {n: t / steps_o for n, (c, t) in kern_o.items()},
         }
     rec["other_workloads"] = others
     print(json.dumps(rec), flush=True)
