@@ -38,7 +38,8 @@ softmax over J (the merge is an exact identity), so the oracle computes the
 softmax over J directly and never merges.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (the static
-routing rules by ``tests/test_static_gate_pins.py``) against hand
+routing rules by ``tests/test_static_gate_pins.py``, the min/max pooled gate
+by ``tests/test_minmax_gate_pins.py``) against hand
 worked examples, library routines (torch SDPA in fp64 for the k >= n and k = 1
 reductions), closed forms and invariants.  The pages print no numeric output
 of the operator itself; the only printed numbers this oracle reproduces are
@@ -322,6 +323,105 @@ def selection_is_valid(Q, K, cu_seqlens, block_size, topk, row, idx_row,
         return True
     kbar = pool_keys_head(K[a:a + L, h, :], L, block_size)
     sc = gate_scores_row(Q[t, h, :], kbar, c)
+    worst_in = min(sc[x] for x in past)
+    others = [sc[i] for i in range(c) if i not in past]
+    if not others:
+        return True
+    best_out = max(others)
+    return bool(best_out - worst_in <= rel * max(abs(best_out), abs(worst_in)))
+
+
+# --------------------------------------------------------------------------
+# min/max pooled gate (the Quest-style variant)
+# --------------------------------------------------------------------------
+# [elamur] "Key points" (related methods): Quest reads as MoBA with smaller
+# blocks and min/max pooling.  Read here as: each block keeps the elementwise
+# maximum and minimum of its keys, and a query scores the block by the largest
+# value q . x can take over the box [kmin, kmax] of the block, which is
+# sum_e max(q_e kmin_e, q_e kmax_e), an upper bound of q . k for every key k
+# of the block.  Selection and attention are those of MoBA.
+
+def pool_minmax_head(K, length, block_size):
+    """Elementwise max and min of each block's keys (one head): K [L, d] ->
+    (kmax [n, d], kmin [n, d]) fp64."""
+    n = num_blocks(length, block_size)
+    d = K.shape[1]
+    kmax = np.zeros((n, d))
+    kmin = np.zeros((n, d))
+    for i in range(n):
+        lo, hi = block_range(i, length, block_size)
+        blk = np.asarray(K[lo:hi], dtype=np.float64)
+        kmax[i] = blk.max(axis=0)
+        kmin[i] = blk.min(axis=0)
+    return kmax, kmin
+
+
+def minmax_scores_row(q, kmax, kmin, c):
+    """Upper-bound affinity of q with every past block i < c:
+    sum over e of max(q_e kmin_e, q_e kmax_e)."""
+    q = np.asarray(q, dtype=np.float64)
+    return np.maximum(q * kmin[:c], q * kmax[:c]).sum(axis=1)
+
+
+def pool_minmax(K, cu_seqlens, block_size):
+    """``pool_minmax_head`` over a packed batch: K [T, H, d] -> kmm [NB, H, 2, d]
+    with kmm[:, :, 0] the block maxima and kmm[:, :, 1] the minima."""
+    T, H, d = K.shape
+    out = []
+    for a, L in sequences(cu_seqlens):
+        n = num_blocks(L, block_size)
+        kb = np.zeros((n, H, 2, d))
+        for h in range(H):
+            kb[:, h, 0], kb[:, h, 1] = pool_minmax_head(K[a:a + L, h, :], L, block_size)
+        out.append(kb)
+    return np.concatenate(out, axis=0) if out else np.zeros((0, H, 2, d))
+
+
+def minmax_gate_reference(Q, K, cu_seqlens, block_size, topk, rows=None):
+    """Block selection with the min/max pooled gate on (token, head) rows:
+    the scores of ``minmax_scores_row``, then the MoBA selection rule
+    (``select_rows``).  Returns dict(rows, idx, gap, near_tie)."""
+    T, H, d = Q.shape
+    rows = _rows_by_head(rows, T, H)
+    R = len(rows)
+    idx = np.full((R, topk), -1, dtype=np.int64)
+    gap = np.full(R, np.inf)
+    near = np.zeros(R, dtype=bool)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    seq_of = np.searchsorted(cu, rows[:, 0], side="right") - 1
+    for s in np.unique(seq_of):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for h in np.unique(rows[seq_of == s, 1]):
+            sel = np.nonzero((seq_of == s) & (rows[:, 1] == h))[0]
+            kmax, kmin = pool_minmax_head(K[a:a + L, h, :], L, block_size)
+            cs = (rows[sel, 0] - a) // block_size
+            for c in np.unique(cs):
+                g = sel[cs == c]
+                S = np.stack([minmax_scores_row(Q[t, h, :], kmax, kmin, int(c))
+                              for t in rows[g, 0]]) if c > 0 else np.zeros((len(g), 0))
+                idx[g], gap[g], near[g] = select_rows(S, int(c), topk)
+    return dict(rows=rows, idx=idx, gap=gap, near_tie=near)
+
+
+def minmax_selection_is_valid(Q, K, cu_seqlens, block_size, topk, row, idx_row,
+                              rel=NEAR_TIE_REL):
+    """``selection_is_valid`` with the min/max pooled scores."""
+    t, h = int(row[0]), int(row[1])
+    s, a, L = _seq_of_token(cu_seqlens, t)
+    c = (t - a) // block_size
+    idx_row = [int(x) for x in idx_row]
+    valid = [x for x in idx_row if x >= 0]
+    if idx_row[len(valid):] != [-1] * (topk - len(valid)):
+        return False
+    if valid != sorted(set(valid)) or not valid or valid[-1] != c:
+        return False
+    past = valid[:-1]
+    if len(past) != min(topk - 1, c) or any(x < 0 or x >= c for x in past):
+        return False
+    if not past:
+        return True
+    kmax, kmin = pool_minmax_head(K[a:a + L, h, :], L, block_size)
+    sc = minmax_scores_row(Q[t, h, :], kmax, kmin, c)
     worst_in = min(sc[x] for x in past)
     others = [sc[i] for i in range(c) if i not in past]
     if not others:
