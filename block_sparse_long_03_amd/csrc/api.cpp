@@ -217,6 +217,45 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
+moba_status moba_pool_minmax(const void* k, int dtype, const int32_t* cu_seqlens,
+                             const int32_t* cu_blocks, int num_seqs, int total_tokens,
+                             int max_seqlen, int total_blocks, int num_heads, int head_dim,
+                             int block_size, float* kminmax, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!k || !kminmax) return MOBA_ERR_INVALID_ARG;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  hipError_t e = timed("pool_minmax", (hipStream_t)stream, [&] {
+    return moba::launch_pool_minmax(k, dtype == MOBA_BF16, g, kminmax, (hipStream_t)stream);
+  });
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
+moba_status moba_gate_topk_minmax(const void* q, int dtype, const float* kminmax,
+                                  const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                  int num_seqs, int total_tokens, int max_seqlen,
+                                  int total_blocks, int num_heads, int head_dim, int block_size,
+                                  int topk, int32_t* block_idx, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (dtype != MOBA_BF16) return MOBA_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !kminmax || !block_idx) return MOBA_ERR_INVALID_ARG;
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  hipError_t e = timed("gate_topk_minmax", (hipStream_t)stream, [&] {
+    return moba::launch_gate_topk_minmax((const uint16_t*)q, kminmax, g, topk, block_idx,
+                                         (hipStream_t)stream);
+  });
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
 moba_status moba_static_select(const int32_t* cu_seqlens, const int32_t* cu_blocks,
                                int num_seqs, int total_tokens, int max_seqlen, int total_blocks,
                                int num_heads, int block_size, int topk, int sink_blocks,

@@ -46,6 +46,9 @@ size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_he
 hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar, hipStream_t st);
 hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const Geo& g,
                             int topk, int32_t* block_idx, hipStream_t st);
+hipError_t launch_pool_minmax(const void* k, bool bf16, const Geo& g, float* kmm, hipStream_t st);
+hipError_t launch_gate_topk_minmax(const uint16_t* q, const float* kmm, const Geo& g, int topk,
+                                   int32_t* block_idx, hipStream_t st);
 hipError_t launch_static_select(const Geo& g, int topk, int sink, int32_t* block_idx,
                                 hipStream_t st);
 

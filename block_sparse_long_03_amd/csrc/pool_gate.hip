@@ -94,6 +94,74 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
   }
 }
 
+// min/max pool: kmm[gb, h, 0, :] = elementwise max of the block's keys,
+// kmm[gb, h, 1, :] = elementwise min (exact: no rounding)
+template <typename T>
+__global__ __launch_bounds__(256) void pool_minmax_kernel(
+    const T* __restrict__ k, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int hd, int D,
+    int block_size, float* __restrict__ kmm) {
+  __shared__ float rmax[32][65];
+  __shared__ float rmin[32][65];
+  const int gb = blockIdx.x;
+  const int col0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 7;
+  const int ty = threadIdx.x >> 3;
+  const int s = seq_of_block(cu_blocks, num_seqs, gb);
+  int start, len;
+  seq_span(cu_seqlens, s, total_tokens, &start, &len);
+  const int local = (gb - cu_blocks[s]) * block_size;
+  const int cnt = min(block_size, len - local);
+
+  float mx[8], mn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { mx[i] = -INFINITY; mn[i] = INFINITY; }
+  if (cnt > 0) {
+    const T* base = k + (size_t)(start + local) * hd + col0 + tx * 8;
+    int j = ty;
+    for (; j + 32 < cnt; j += 64) {
+      float v0[8], v1[8];
+      load8<T>(base + (size_t)j * hd, v0);
+      load8<T>(base + (size_t)(j + 32) * hd, v1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mx[i] = fmaxf(mx[i], fmaxf(v0[i], v1[i]));
+        mn[i] = fminf(mn[i], fminf(v0[i], v1[i]));
+      }
+    }
+    for (; j < cnt; j += 32) {
+      float v0[8];
+      load8<T>(base + (size_t)j * hd, v0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { mx[i] = fmaxf(mx[i], v0[i]); mn[i] = fminf(mn[i], v0[i]); }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { rmax[ty][tx * 8 + i] = mx[i]; rmin[ty][tx * 8 + i] = mn[i]; }
+  __syncthreads();
+  for (int stride = 16; stride >= 1; stride >>= 1) {
+    if (ty < stride) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        rmax[ty][tx * 8 + i] = fmaxf(rmax[ty][tx * 8 + i], rmax[ty + stride][tx * 8 + i]);
+        rmin[ty][tx * 8 + i] = fminf(rmin[ty][tx * 8 + i], rmin[ty + stride][tx * 8 + i]);
+      }
+    }
+    __syncthreads();
+  }
+  if (ty == 0) {
+    // column col0 + 8 tx + i of the [H * D] row is (head, dim) = divmod(col, D)
+    const int col = col0 + tx * 8;
+    const int h = col / D, e = col - h * D;
+    float* dst = kmm + ((size_t)gb * (hd / D) + h) * 2 * D + e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dst[i] = cnt > 0 ? rmax[0][tx * 8 + i] : 0.f;
+      dst[D + i] = cnt > 0 ? rmin[0][tx * 8 + i] : 0.f;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gate + top-k
 // ---------------------------------------------------------------------------
@@ -135,25 +203,41 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
 // into three bf16 parts and the three products summed by
 // v_mfma_f32_32x32x16_bf16 (products exact, fp32 accumulation); each of the
 // 4 waves owns one 32 x 32 tile (block tile w).
-template <int D>
+// bf16 fragment with every negative element (sign bit set) zeroed (NEG false)
+// or every non-negative one zeroed (NEG true): q+ and q- exactly
+template <bool NEG>
+__device__ __forceinline__ bf16x8 sign_part(const bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = ((w[i] >> 15) & 0x00010001u) * 0xffffu;  // 0xffff where negative
+    w[i] &= NEG ? m : ~m;
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// QUEST: kbar rows are [kmax (D), kmin (D)] and the score is
+// q+ . kmax + q- . kmin = sum_e max(q_e kmin_e, q_e kmax_e)
+template <int D, bool QUEST>
 __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
                                                  const float* __restrict__ kbar, int H, int h,
                                                  int gblk0, int nb, int total_blocks,
                                                  float (*ss)[kGateStride], int col0, int w,
                                                  int lane) {
+  constexpr int KD = QUEST ? 2 * D : D;  // length of a kbar row
   const int l32 = lane & 31, hf = lane >> 5;
   const int bt = w & 3, tt = w >> 2;
   const int j = 32 * bt + l32;  // block of this lane's A rows
   const bool ok = j < nb && gblk0 + j < total_blocks;
   // lanes past the chunk read block gblk0 (always valid) and zero it, so the
   // loads carry no branch and can all be in flight together
-  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * D + 8 * hf;
+  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * KD + 8 * hf;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  constexpr int KH = D / 32;  // k-steps per half (loads of a half in flight together)
+  constexpr int KH = D / 32;  // k-steps per group (loads of a group in flight together)
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < KD / (16 * KH); ++half) {
   f32x4 xa[KH], xb[KH];
 #pragma unroll
   for (int kk = 0; kk < KH; ++kk) {
@@ -174,9 +258,14 @@ __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
       mid[e] = b;
       lo[e] = cc;
     }
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qfrag[ks], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qfrag[ks], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qfrag[ks], acc, 0, 0, 0);
+    bf16x8 qb;
+    if constexpr (QUEST)
+      qb = ks < D / 16 ? sign_part<false>(qfrag[ks]) : sign_part<true>(qfrag[ks - D / 16]);
+    else
+      qb = qfrag[ks];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qb, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qb, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qb, acc, 0, 0, 0);
   }
   }
   // acc[r] = score of block 32 bt + 8 (r / 4) + 4 hf + (r % 4) for token 32 tt + (lane & 31)
@@ -234,13 +323,14 @@ __device__ __forceinline__ void gate_scores_valu(const float (*qs)[D + 4], float
 // to 256 at a time; each wave then selects for its 8 rows (see the two
 // selection paths below); among keys equal to the threshold the lower block
 // indices win.
-template <typename T, int D>
-__global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void gate_topk_kernel(
+template <typename T, int D, bool QUEST>
+__global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu(QUEST && D > 64 ? 2 : 4))) void gate_topk_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
     int total_tokens, int total_blocks, int tiles_per_seq, int H, int block_size, int topk,
     int32_t* __restrict__ block_idx) {
   constexpr bool kMfma = sizeof(T) == 2;
+  static_assert(kMfma || !QUEST, "the min/max pooled gate runs on the bf16 path");
   __shared__ float ss[kGateRows][kGateStride];
   __shared__ uint32_t skey[kGateWaves][64];
   __shared__ int32_t sidx[kGateWaves][64];
@@ -285,7 +375,7 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
       const int nspan = min(kGateSpan, c - base);
       if constexpr (kMfma) {
         for (int cb = 0; cb < nspan; cb += kGateChunk)
-          gate_scores_mfma<D>(qfrag, kbar, H, h, gb0 + base + cb, min(kGateChunk, nspan - cb),
+          gate_scores_mfma<D, QUEST>(qfrag, kbar, H, h, gb0 + base + cb, min(kGateChunk, nspan - cb),
                               total_blocks, ss, cb, w, lane);
         __syncthreads();
       } else {
@@ -615,6 +705,39 @@ hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar,
   return hipGetLastError();
 }
 
+hipError_t launch_pool_minmax(const void* k, bool bf16, const Geo& g, float* kmm,
+                              hipStream_t st) {
+  if (g.total_blocks == 0) return hipSuccess;
+  const int hd = g.num_heads * g.head_dim;
+  dim3 grid(g.total_blocks, hd / 64);
+  if (bf16)
+    hipLaunchKernelGGL(pool_minmax_kernel<uint16_t>, grid, dim3(256), 0, st,
+                       (const uint16_t*)k, g.cu_seqlens, g.cu_blocks, g.num_seqs,
+                       g.total_tokens, hd, g.head_dim, g.block_size, kmm);
+  else
+    hipLaunchKernelGGL(pool_minmax_kernel<float>, grid, dim3(256), 0, st, (const float*)k,
+                       g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, hd, g.head_dim,
+                       g.block_size, kmm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_topk_minmax(const uint16_t* q, const float* kmm, const Geo& g, int topk,
+                                   int32_t* block_idx, hipStream_t st) {
+  if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
+  const int tiles = (g.max_seqlen + kGateRows - 1) / kGateRows;
+  dim3 grid(g.num_seqs * tiles, g.num_heads);
+  dim3 block(kGateWaves * 64);
+  if (g.head_dim == 128)
+    hipLaunchKernelGGL((gate_topk_kernel<uint16_t, 128, true>), grid, block, 0, st, q, kmm,
+                       g.cu_seqlens, g.cu_blocks, g.total_tokens, g.total_blocks, tiles,
+                       g.num_heads, g.block_size, topk, block_idx);
+  else
+    hipLaunchKernelGGL((gate_topk_kernel<uint16_t, 64, true>), grid, block, 0, st, q, kmm,
+                       g.cu_seqlens, g.cu_blocks, g.total_tokens, g.total_blocks, tiles,
+                       g.num_heads, g.block_size, topk, block_idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const Geo& g,
                             int topk, int32_t* block_idx, hipStream_t st) {
   if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
@@ -622,7 +745,7 @@ hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const G
   dim3 grid(g.num_seqs * tiles, g.num_heads);
   dim3 block(kGateWaves * 64);
 #define MOBA_GATE(T, D)                                                                   \
-  hipLaunchKernelGGL((gate_topk_kernel<T, D>), grid, block, 0, st, (const T*)q, kbar,     \
+  hipLaunchKernelGGL((gate_topk_kernel<T, D, false>), grid, block, 0, st, (const T*)q, kbar, \
                      g.cu_seqlens, g.cu_blocks, g.total_tokens, g.total_blocks, tiles,    \
                      g.num_heads,                                                         \
                      g.block_size, topk, block_idx)

@@ -28,7 +28,7 @@ MOBA_F32 = 0
 MOBA_BF16 = 1
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
-           "moba_gate_topk", "moba_static_select", "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select", "moba_attn_workspace_bytes", "moba_attn_fwd",
            "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
            "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
            "moba_profiler_names", "moba_profiler_destroy"]
@@ -66,6 +66,10 @@ def lib():
     L.moba_pool_keys.argtypes = [vp, i32] + geo + [vp, vp]
     L.moba_gate_topk.restype = i32
     L.moba_gate_topk.argtypes = [vp, i32, vp] + geo + [i32, vp, vp]
+    L.moba_pool_minmax.restype = i32
+    L.moba_pool_minmax.argtypes = [vp, i32] + geo + [vp, vp]
+    L.moba_gate_topk_minmax.restype = i32
+    L.moba_gate_topk_minmax.argtypes = [vp, i32, vp] + geo + [i32, vp, vp]
     L.moba_static_select.restype = i32
     L.moba_static_select.argtypes = [vp, vp] + [i32] * 8 + [vp, vp]
     L.moba_attn_workspace_bytes.restype = sz
@@ -171,6 +175,27 @@ def moba_gate_topk(q, kbar, geom, topk, block_idx=None, stream=None):
         block_idx = torch.empty((geom.total_tokens, H, topk), dtype=torch.int32, device=q.device)
     _check("moba_gate_topk", lib().moba_gate_topk(
         _ptr(q), _dtype_code(q.dtype), _ptr(kbar), *geom.args(H, d), int(topk),
+        _ptr(block_idx), _stream(stream)))
+    return block_idx
+
+
+def moba_pool_minmax(k, geom, kminmax=None, stream=None):
+    """Elementwise block max and min of the keys: kminmax [NB, H, 2, d] fp32."""
+    H, d = _qkv_shape(k, geom)
+    if kminmax is None:
+        kminmax = torch.empty((geom.total_blocks, H, 2, d), dtype=torch.float32, device=k.device)
+    _check("moba_pool_minmax", lib().moba_pool_minmax(
+        _ptr(k), _dtype_code(k.dtype), *geom.args(H, d), _ptr(kminmax), _stream(stream)))
+    return kminmax
+
+
+def moba_gate_topk_minmax(q, kminmax, geom, topk, block_idx=None, stream=None):
+    """Causal top-k with the min/max pooled score (bf16 q)."""
+    H, d = _qkv_shape(q, geom)
+    if block_idx is None:
+        block_idx = torch.empty((geom.total_tokens, H, topk), dtype=torch.int32, device=q.device)
+    _check("moba_gate_topk_minmax", lib().moba_gate_topk_minmax(
+        _ptr(q), _dtype_code(q.dtype), _ptr(kminmax), *geom.args(H, d), int(topk),
         _ptr(block_idx), _stream(stream)))
     return block_idx
 
@@ -294,6 +319,16 @@ def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=N
     return out, lse, idx
 
 
+def forward_minmax(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):
+    """MoBA with the min/max pooled gate: pool_minmax -> gate -> sparse
+    attention.  Returns (out, lse, block_idx)."""
+    kmm = moba_pool_minmax(k, geom, stream=stream)
+    idx = moba_gate_topk_minmax(q, kmm, geom, topk, stream=stream)
+    out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
+                             workspace=workspace, stream=stream)
+    return out, lse, idx
+
+
 def forward_static(q, k, v, geom, topk, sink_blocks, scale, out_dtype=None, workspace=None,
                    stream=None):
     """Attention through a static gate (sliding window / sink + window / full):
@@ -309,3 +344,29 @@ def dense(q, k, v, geom, scale, out_dtype=None, workspace=None, stream=None):
     """Dense causal attention with the library's own kernel.  Returns (out, lse)."""
     return moba_dense_causal_fwd(q, k, v, geom, scale, out_dtype=out_dtype,
                                  workspace=workspace, stream=stream)
+
+
+def hybrid_schedule(num_layers, full_last):
+    """Attention mode of each layer in the layer-wise hybrid: MoBA for the
+    first num_layers - full_last layers, full attention for the last
+    full_last ("MoBA: Learned Block Sparsity for Long-Context Attention",
+    section "Why the Change Is Plausible": switching the last layers to full
+    attention; the hybrid mode of the elamur.ai summary, "Key points")."""
+    if not 0 <= full_last <= num_layers:
+        raise ValueError("full_last must lie in [0, num_layers]")
+    return ["moba"] * (num_layers - full_last) + ["full"] * full_last
+
+
+def layer_forward(mode, q, k, v, geom, topk, scale, out_dtype=None, workspace=None,
+                  stream=None):
+    """One attention layer in the given hybrid mode: "moba" (pool, gate,
+    sparse attention) or "full" (the dense causal kernel).  Returns
+    (out, lse)."""
+    if mode == "moba":
+        out, lse, _ = forward(q, k, v, geom, topk, scale, out_dtype=out_dtype,
+                              workspace=workspace, stream=stream)
+        return out, lse
+    if mode == "full":
+        return dense(q, k, v, geom, scale, out_dtype=out_dtype, workspace=workspace,
+                     stream=stream)
+    raise ValueError(f"unknown attention mode {mode!r}")

@@ -119,6 +119,39 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
                            void* stream);
 
 /*
+ * Min/max pooling of the keys (the pooled representation of the min/max
+ * gate below).  "MoBA: Mixture of Block Attention for Long-Context LLMs"
+ * (research.elamur.ai), "Key points": Quest reads as MoBA with smaller blocks
+ * and min/max pooling.
+ *   kminmax[b, h, 0, :] = elementwise max of k[t, h, :] over the tokens t of
+ *   block b;  kminmax[b, h, 1, :] = elementwise min.  Exact (no rounding).
+ *   k        [total_tokens, num_heads, head_dim], dtype
+ *   kminmax  [total_blocks, num_heads, 2, head_dim] fp32, written in full
+ */
+moba_status moba_pool_minmax(const void* k, int dtype, const int32_t* cu_seqlens,
+                             const int32_t* cu_blocks, int num_seqs, int total_tokens,
+                             int max_seqlen, int total_blocks, int num_heads, int head_dim,
+                             int block_size, float* kminmax, void* stream);
+
+/*
+ * Gate and causal top-k with the min/max pooled score.  As moba_gate_topk
+ * (same causality, forced own block counted in topk, ties to the lower
+ * block index, same block_idx format) with the score of past block i
+ *   s_i = sum_e max(q_e * kmin_i[e], q_e * kmax_i[e])
+ *       = the largest q . x over the box [kmin_i, kmax_i] of block i,
+ * an upper bound of q . k for every key k of the block (the reading of
+ * min/max pooling adopted here; the page gives no formula).
+ *   kminmax  output of moba_pool_minmax
+ * bf16 inputs only (MOBA_ERR_UNSUPPORTED for MOBA_F32).  Products are exact,
+ * accumulation fp32.
+ */
+moba_status moba_gate_topk_minmax(const void* q, int dtype, const float* kminmax,
+                                  const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                  int num_seqs, int total_tokens, int max_seqlen,
+                                  int total_blocks, int num_heads, int head_dim, int block_size,
+                                  int topk, int32_t* block_idx, void* stream);
+
+/*
  * Static routing: a fixed gate in place of moba_gate_topk.
  * "MoBA: Learned Block Sparsity for Long-Context Attention", section "Why
  * the Change Is Plausible" (static sparse patterns as special cases of the

@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
@@ -99,6 +99,26 @@ def test_static_select_arguments(L):
     assert static(L, topk=65) == U
     assert static(L, B=96) == U
     assert static(L, T=0, maxL=0, NB=0, idx=None) == moba.MOBA_OK   # empty batch: nothing to do
+
+
+def test_minmax_arguments(L):
+    E, U = moba.MOBA_ERR_INVALID_ARG, moba.MOBA_ERR_UNSUPPORTED
+    g = [GEO[x] for x in ("cu", "cb", "S", "T", "maxL", "NB", "H", "d", "B")]
+    assert L.moba_pool_minmax(None, 1, *g, FAKE, None) == E
+    assert L.moba_pool_minmax(FAKE, 1, *g, None, None) == E
+    assert L.moba_pool_minmax(FAKE, 1, *g[:7], 96, g[8], FAKE, None) == U
+    assert L.moba_gate_topk_minmax(FAKE, 0, FAKE, *g, 3, FAKE, None) == U   # fp32: bf16 only
+    assert L.moba_gate_topk_minmax(FAKE, 1, None, *g, 3, FAKE, None) == E
+    assert L.moba_gate_topk_minmax(FAKE, 1, FAKE, *g, 0, FAKE, None) == E
+
+
+def test_hybrid_schedule():
+    assert moba.hybrid_schedule(32, 3) == ["moba"] * 29 + ["full"] * 3
+    assert moba.hybrid_schedule(4, 0) == ["moba"] * 4
+    with pytest.raises(ValueError):
+        moba.hybrid_schedule(4, 5)
+    with pytest.raises(ValueError):
+        moba.layer_forward("sparse", None, None, None, None, 3, 0.1)
 
 
 def test_unsupported(L):
