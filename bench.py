@@ -136,21 +136,25 @@ def cpu_baseline(x, w, rows_target, seconds):
     }
 
 
-def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, sink=None):
+def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, gate="mean"):
     """Times `steps` MoBA layers (pool, gate + top-k, attention) on one
     workload after `warmup` untimed ones, then the library's own dense causal
-    kernel `dense_reps` times.  With `sink` set, the learned gate is replaced
-    by the static routing of moba_static_select (sink 0: sliding window).
-    Returns the inputs (if keep), the geometry, ms per step, per-stage
-    HIP-event totals, dense ms and dense stages."""
-    gate = "learned" if sink is None else f"static sink {sink}"
+    kernel `dense_reps` times.  `gate` picks the routing: "mean" (the MoBA
+    gate on mean-pooled keys), "minmax" (min/max pooled keys), "window" or
+    "sinkN" (static routing with N initial blocks).  Returns the inputs (if
+    keep), the geometry, ms per step, per-stage HIP-event totals, dense ms and
+    dense stages."""
+    sink = 0 if gate == "window" else int(gate[4:]) if gate.startswith("sink") else None
+    if sink is None and gate not in ("mean", "minmax"):
+        raise SystemExit(f"unknown gate {gate!r}")
     print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} d{w.head_dim} B{w.block_size} "
           f"k{w.topk} gate {gate}", file=sys.stderr, flush=True)
     x = inputs.make_inputs(w, device=dev)
     geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
     H, d = w.heads, w.head_dim
     dt = moba.MOBA_BF16 if w.dtype == "bf16" else moba.MOBA_F32
-    kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty((geom.total_blocks, H, 2 if gate == "minmax" else 1, d),
+                       dtype=torch.float32, device=dev)
     idx = torch.empty((geom.total_tokens, H, w.topk), dtype=torch.int32, device=dev)
     out = torch.empty_like(x["q"])
     lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=dev)
@@ -160,9 +164,12 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     q, k, v = x["q"], x["k"], x["v"]
 
     def step():
-        if sink is None:
+        if gate == "mean":
             moba.moba_pool_keys(k, geom, kbar=kbar)
             moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+        elif gate == "minmax":
+            moba.moba_pool_minmax(k, geom, kminmax=kbar)
+            moba.moba_gate_topk_minmax(q, kbar, geom, w.topk, block_idx=idx)
         else:
             moba.moba_static_select(geom, H, w.topk, sink, block_idx=idx)
         moba.moba_attn_fwd(q, k, v, geom, w.topk, idx, w.scale, out=out, lse=lse, workspace=ws)
@@ -224,10 +231,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--also", default="32k,1m:window,1m:sink1",
+    ap.add_argument("--also", default="32k,1m:minmax,1m:window,1m:sink1",
                     help="comma-separated extra workloads reported under other_workloads "
-                         "(ms/layer, TFLOP/s, dense, speedup); NAME:window or NAME:sinkN "
-                         "replaces the learned gate by static routing; empty for none")
+                         "(ms/layer, TFLOP/s, dense, speedup); NAME:minmax uses the min/max "
+                         "pooled gate, NAME:window or NAME:sinkN static routing; empty for none")
     ap.add_argument("--also-steps", type=int, default=20,
                     help="timed steps of the extra workloads (3 above 256K tokens)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -320,26 +327,20 @@ def main():
     others = {}
     for name in [n for n in args.also.split(",") if n and n != w.name]:
         wname, _, gate = name.partition(":")
-        sink = None
-        if gate == "window":
-            sink = 0
-        elif gate.startswith("sink"):
-            sink = int(gate[4:])
-        elif gate:
-            raise SystemExit(f"unknown gate {gate!r} in --also")
+        gate = gate or "mean"
         wo = inputs.WORKLOADS[wname]
         steps_o = args.also_steps if wo.total_tokens <= (1 << 18) else min(args.also_steps, 3)
-        # the dense time of a workload is measured once, with its learned-gate line
-        dense_reps_o = 2 if (args.dense_reps and sink is None) else 0
+        # gate variants of the headline workload reuse its dense time
+        dense_reps_o = 2 if (args.dense_reps and wname != w.name) else 0
         _, _, ms_o2, kern_o, dense_o, _ = measure(torch, inputs, moba, wo, dev, steps_o,
-                                                  max(1, args.warmup), dense_reps_o, sink=sink)
+                                                  max(1, args.warmup), dense_reps_o, gate=gate)
         if dense_o is None and wname == w.name:
             dense_o = dense_ms
         pairs_o, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
         n_ho, ms_ho = kern_o.get("attn_hist", (0, 0.0))
         hist_o = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)[1]
         others[name] = {
-            "config": {"workload": wname, "gate": gate or "learned",
+            "config": {"workload": wname, "gate": gate,
                        "seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": wo.head_dim,
                        "block_size": wo.block_size, "topk": wo.topk},
             "steps": steps_o,
