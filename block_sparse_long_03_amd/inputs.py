@@ -61,6 +61,10 @@ WORKLOADS = {
     "32k": Workload("32k", (32768,), 32, 128, 256, 32, "bf16", lowrank_bias=True, index=2),
     "varlen": Workload("varlen", (65536, 32768, 16384, 16384), 32, 128, 4096, 12, "bf16", index=3),
     "1m": Workload("1m", (1 << 20,), 32, 128, 4096, 12, "bf16", index=4),
+    # constant sparsity at 10M tokens: the block count of the 1M workload
+    # (256) kept, so B grows to 40960; 4 heads = one GPU's share of 32 heads
+    # sharded by head over 8 GPUs
+    "10m": Workload("10m", (10 << 20,), 4, 128, 40960, 12, "bf16", index=5),
 }
 
 

@@ -149,8 +149,27 @@ def test_moba_1m_sampled(dev):
     st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx,
                                    heads=[5])
     print("1m head 5 selections", st)
-    # every row: ascending past blocks, then the own block, then -1 padding,
-    # min(k, c + 1) entries
+    _check_rows_valid(w, idx, out, lse)
+
+
+def test_moba_10m_sampled(dev):
+    """Constant sparsity at 10M tokens (B 40960 keeps the 1M workload's 256
+    blocks), one GPU's 4-head share: outputs and selections on 64 seeded
+    rows of two heads, causal validity of every selection row."""
+    w = inputs.WORKLOADS["10m"]
+    x, geom, out, lse, idx = _run(w, dev)
+    rows = inputs.sample_rows(w, 32, heads=[0, 3])
+    st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
+                                w.scale, out, lse, idx, rows, parity.BF16_TOL)
+    print("10m", st)
+    _check_rows_valid(w, idx, out, lse)
+    del x, out, lse, idx
+    torch.cuda.empty_cache()
+
+
+def _check_rows_valid(w, idx, out, lse):
+    """Every row: ascending past blocks, then the own block, then -1 padding,
+    min(k, c + 1) entries; finite outputs (one sequence)."""
     T, H, k = idx.shape
     c = (torch.arange(T, device=idx.device) // w.block_size).view(T, 1, 1)
     valid = idx >= 0
