@@ -39,7 +39,8 @@ softmax over J directly and never merges.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (the static
 routing rules by ``tests/test_static_gate_pins.py``, the min/max pooled gate
-by ``tests/test_minmax_gate_pins.py``) against hand
+by ``tests/test_minmax_gate_pins.py``, the backward pass by
+``tests/test_backward_pins.py``) against hand
 worked examples, library routines (torch SDPA in fp64 for the k >= n and k = 1
 reductions), closed forms and invariants.  The pages print no numeric output
 of the operator itself; the only printed numbers this oracle reproduces are
@@ -329,6 +330,62 @@ def selection_is_valid(Q, K, cu_seqlens, block_size, topk, row, idx_row,
         return True
     best_out = max(others)
     return bool(best_out - worst_in <= rel * max(abs(best_out), abs(worst_in)))
+
+
+# --------------------------------------------------------------------------
+# backward pass: gradients of the attention over the selected tokens
+# --------------------------------------------------------------------------
+# [wispaper] "The Change" and [elamur] "Key points": MoBA is trained end to end
+# with the block selection made by a hard top-k, so gradients reach q, K and V
+# through the softmax attention over the selected tokens only; the selection
+# itself is not differentiated.  For one (sequence, head), with M the token
+# mask of the selection (step 4), X = scale Q K^T on M (-inf elsewhere),
+# P = softmax_rows(X), O = P V and an upstream gradient dO:
+#   dV = P^T dO
+#   dP = dO V^T
+#   dS = P * (dP - rowsum(dO * O))        (softmax Jacobian, elementwise *)
+#   dQ = scale dS K,   dK = scale dS^T Q
+
+def token_mask(idx_seq, L, block_size):
+    """Token mask of one sequence from its per-token selections idx_seq
+    [L, topk]: M[t, j] = j is in a selected block of t and j <= t (step 4)."""
+    M = np.zeros((L, L), dtype=bool)
+    for t in range(L):
+        M[t, attended_tokens(idx_seq[t], t, block_size)] = True
+    return M
+
+
+def attention_backward_masked(Q, K, V, dO, M, scale):
+    """Gradients of O = softmax(scale Q K^T on M) V for one head:
+    Q, K, V, dO [L, d]; M [L, L] bool with at least one True per row.
+    Returns (dQ, dK, dV) fp64."""
+    Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+    X = np.where(M, scale * (Q @ K.T), -np.inf)
+    mx = X.max(axis=1, keepdims=True)
+    W = np.exp(X - mx)
+    P = W / W.sum(axis=1, keepdims=True)
+    O = P @ V
+    dV = P.T @ dO
+    dP = dO @ V.T
+    Drow = (dO * O).sum(axis=1, keepdims=True)
+    dS = P * (dP - Drow)
+    return scale * dS @ K, scale * dS.T @ Q, dV
+
+
+def moba_backward_reference(Q, K, V, dO, cu_seqlens, block_size, idx, scale, heads=None):
+    """dQ, dK, dV [T, H, d] fp64 of the attention over the given selections
+    idx [T, H, topk] (the heads listed, default all; other heads are zero)."""
+    T, H, d = Q.shape
+    dQ, dK, dV = (np.zeros((T, H, d)) for _ in range(3))
+    for h in (range(H) if heads is None else heads):
+        for a, L in sequences(cu_seqlens):
+            if L == 0:
+                continue
+            M = token_mask(idx[a:a + L, h], L, block_size)
+            g = attention_backward_masked(Q[a:a + L, h], K[a:a + L, h], V[a:a + L, h],
+                                          dO[a:a + L, h], M, scale)
+            dQ[a:a + L, h], dK[a:a + L, h], dV[a:a + L, h] = g
+    return dQ, dK, dV
 
 
 # --------------------------------------------------------------------------
