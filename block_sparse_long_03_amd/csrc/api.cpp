@@ -132,6 +132,38 @@ long long hist_tiles_bound(long long T, long long NB, long long H, long long B, 
   return (e + tq - 1) / tq + H * NB;
 }
 
+// Backward workspace: the bucket lists and tiles of 128 queries, and
+// Dq = rowsum(dO * O) per (token, head).
+struct BwdWorkspace {
+  size_t counts, offsets, tile_offsets, list, tile_info, dvec, total;
+};
+
+constexpr int kBwdTileQ = 128;
+
+long long bwd_tiles_bound(long long T, long long NB, long long H, long long topk) {
+  if (topk < 2) return 0;
+  return (T * H * (topk - 1) + kBwdTileQ - 1) / kBwdTileQ + H * NB;
+}
+
+BwdWorkspace bwd_workspace_layout(long long T, long long NB, long long H, long long topk) {
+  BwdWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t nkeys = (size_t)(H * NB);
+  w.counts = take(nkeys * 4);
+  w.offsets = take((nkeys + 1) * 4);
+  w.tile_offsets = take((nkeys + 1) * 4);
+  w.list = take((size_t)(T * H * (topk > 1 ? topk - 1 : 1)) * 4);
+  w.tile_info = take((size_t)bwd_tiles_bound(T, NB, H, topk) * 16);
+  w.dvec = take((size_t)(T * H) * 4);
+  w.total = off;
+  return w;
+}
+
 AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long long H,
                                     long long D, long long B, long long topk) {
   AttnWorkspace w{};
@@ -370,6 +402,75 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
   if ((e = timed("merge", s, [&] {
          return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, vmax, out,
                                    out_bf16, lse, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  return MOBA_OK;
+}
+
+size_t moba_attn_bwd_workspace_bytes(int dtype, int total_tokens, int total_blocks,
+                                     int num_heads, int head_dim, int block_size, int topk) {
+  if (dtype != MOBA_BF16 || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||
+      (head_dim != 64 && head_dim != 128) || block_size < 64 || block_size % 64 != 0 ||
+      check_topk(total_tokens, topk) != MOBA_OK)
+    return 0;
+  return moba::bwd_workspace_layout(total_tokens, total_blocks, num_heads, topk).total + kAlign;
+}
+
+moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                          int out_dtype, const void* dout, const float* lse, int dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                          int total_tokens, int max_seqlen, int total_blocks, int num_heads,
+                          int head_dim, int block_size, int topk, const int32_t* block_idx,
+                          float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (dtype != MOBA_BF16) return MOBA_ERR_UNSUPPORTED;
+  if (!dtype_ok(out_dtype)) return MOBA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !block_idx || !dq || !dk || !dv || !workspace)
+    return MOBA_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace % kAlign != 0) return MOBA_ERR_INVALID_ARG;
+  const moba::BwdWorkspace L =
+      moba::bwd_workspace_layout(total_tokens, total_blocks, num_heads, topk);
+  if (workspace_bytes < L.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+  const long long tiles = moba::bwd_tiles_bound(total_tokens, total_blocks, num_heads, topk);
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  if (tiles >= (1LL << 31) || hist_entries_bound(g, topk) / 4 >= (1LL << 31))
+    return MOBA_ERR_UNSUPPORTED;
+  char* ws = (char*)workspace;
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* tile_offsets = (int32_t*)(ws + L.tile_offsets);
+  int32_t* list = (int32_t*)(ws + L.list);
+  int4* tile_info = (int4*)(ws + L.tile_info);
+  float* dvec = (float*)(ws + L.dvec);
+  const uint16_t *qb = (const uint16_t*)q, *kb = (const uint16_t*)k, *vb = (const uint16_t*)v,
+                 *gb = (const uint16_t*)dout;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = timed("bwd_prep", s, [&] {
+         return moba::launch_bwd_prep(out, out_dtype == MOBA_F32, gb, g, dvec, dq, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = timed("bucket", s, [&] {
+         return moba::launch_bucket(block_idx, g, topk, moba::kBwdTileQ, counts, offsets,
+                                    tile_offsets, list, tile_info, tiles, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = timed("bwd_kv", s, [&] {
+         return moba::launch_bwd_kv(qb, kb, vb, gb, lse, dvec, g, topk, softmax_scale, list,
+                                    offsets, dk, dv, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = timed("bwd_q", s, [&] {
+         return moba::launch_bwd_q(qb, kb, vb, gb, lse, dvec, g, topk, softmax_scale, list,
+                                   tile_info, tiles, dq, s);
        })) != hipSuccess)
     return hip_fail(e);
   return MOBA_OK;

@@ -1,0 +1,642 @@
+// Backward of the MoBA block attention on gfx950: bf16 MFMA, fp32 accumulation.
+//
+// The block selection is a hard top-k and is not differentiated ("MoBA:
+// Learned Block Sparsity for Long-Context Attention", "The Change"; the
+// elamur.ai summary, "Key points": trained end to end with the gate's
+// choice held fixed); gradients reach q, K and V through the softmax
+// attention over each query's selected tokens.  With P = exp(scale q.k - lse)
+// (lse from the forward pass, so P is the final softmax weight of the pair),
+// Dq = dO_q . O_q and dP = dO_q . v_k:
+//   dV_k += P dO_q,   dS = P (dP - Dq),   dK_k += scale dS q,   dQ_q += scale dS k
+//
+// Three kernels:
+//   bwd_prep:  Dq = rowsum(dO * O) per (token, head) and dq = 0.
+//   bwd_kv:    KV-centric.  A workgroup owns 32 keys per wave of one (head,
+//              KV block) and streams every query that attends them: the
+//              block's historical list (queries that selected it), then the
+//              own-block queries at or after its first key (causal mask).
+//              dK and dV stay in registers for the whole stream and are
+//              written once: no atomics, deterministic.
+//   bwd_q:     the forward's tiles (a (head, block) list tile of gathered
+//              queries, or an own-block query tile) against the block's keys
+//              in 64-key chunks; each wave keeps its 32 queries' dQ in
+//              registers and adds it to the fp32 dq once per tile with
+//              coalesced atomics (a query gets at most topk additions).
+//
+// Products:
+//   bwd_kv:  S = Q K^T and dP = dO V^T (A = query rows from LDS, B = the
+//            wave's key rows in registers), then dV^T += dO^T P and
+//            dK^T += Q^T dS, whose A operands (dims x queries) come from the
+//            row-major query tiles through the LDS transpose read
+//            (ds_read_b64_tr_b16).
+//   bwd_q:   S^T = K Q^T and dP^T = V dO^T (A = key rows from LDS, B = the
+//            wave's query rows in registers), then dQ^T += K^T dS^T with K^T
+//            again from the transpose read.
+// In both, the C layout of the first products (lane = one column, 16 rows
+// in the MFMA row order 8(r/4) + 4(lane/32) + r%4) is used as the B operand
+// of the last ones directly: the A operand's k index follows the same order,
+// which the transpose read produces by picking the rows it gathers.
+#include "common.h"
+#include "launch.h"
+
+namespace moba {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void_b;
+
+enum { kBwdHist = 0, kBwdOwn = 1 };
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdKeysPerWave = 32;
+constexpr int kBwdKeysPerWg = kBwdWaves * kBwdKeysPerWave;  // 128
+constexpr int kBwdQTile = 32;                               // queries per bwd_kv step
+constexpr int kBwdChunk = 64;                               // keys per bwd_q step
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;   // [T, H] natural log, from the forward pass
+  const float* dvec;  // [T, H] rowsum(dO * O)
+  const int32_t* cu_seqlens;
+  const int32_t* cu_blocks;
+  int num_seqs, total_tokens, H, block_size, topk, NB;
+  int tiles_per_unit;  // bwd_q own: query tiles per block
+  int units_per_seq;   // bwd_q own: max blocks per sequence
+  int kgroups;         // bwd_kv: key groups per block (block_size / 128)
+  float scale, scale2;  // softmax scale, scale * log2(e)
+  const int32_t* list;     // per (head, block) entries token * topk + slot
+  const int32_t* offsets;  // list range of key h * NB + gb
+  const int4* tile_info;   // bwd_q historical tiles
+  float* dq;
+  float* dk;
+  float* dv;
+};
+
+// 16-byte segment swizzle of a tile row: rows of 256 B (d = 128) or 128 B
+// (d = 64).  A 16-row run of operand row reads and a transpose read (4
+// consecutive rows x 32 bytes per 16 lanes) both hit distinct banks.
+template <int ROWB>
+__device__ __forceinline__ int bswz(int row) {
+  if (ROWB == 256) return ((row & 7) << 1) | ((row >> 3) & 1);
+  const int m = (row >> 1) & 7;
+  return ((m & 3) << 1) | (m >> 2);
+}
+
+__device__ __forceinline__ void bwd_dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_b*)dst, 16, 0, 0);
+}
+
+// A operand X^T (dims 32 dt .. + 31 as rows, 16 tile rows R0 .. R0 + 15 as k)
+// from a row-major bf16 tile X: the k order is the MFMA output row order, so
+// it pairs with a B operand taken from an MFMA result's registers 8 s .. 8 s + 7.
+// off[0] / off[1] are the lane's byte offsets of its two 8-byte reads
+// relative to row R0 (a multiple of 16).
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile_r0, uint32_t off0, uint32_t off1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile_r0 + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile_r0 + off1));
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// the lane's two transpose-read offsets for dims 32 dt .. 32 dt + 31: lane
+// l of group g = l / 16 (index i = l % 16) points at row 4 (g / 2) + i / 4
+// (+ 8 for the second read) and dims 32 dt + 16 (g % 2) + 4 (i % 4) .. + 3;
+// the read hands lane l the four values of dim 32 dt + l % 32 at rows
+// 4 (l / 32) + 0..3 (resp. 8 + ...), i.e. k = 8 (l / 32) + 0..7 in MFMA order.
+template <int ROWB>
+__device__ __forceinline__ uint32_t tr_offset(int lane, int dt, int second) {
+  const int g = lane >> 4, i = lane & 15;
+  const int row = 4 * (g >> 1) + (i >> 2) + 8 * second;
+  const int col_b = 2 * (32 * dt + 16 * (g & 1) + 4 * (i & 3));
+  const int seg = col_b >> 4;
+  return (uint32_t)(row * ROWB + ((seg ^ bswz<ROWB>(row)) << 4) + (col_b & 15));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+// bf16 B fragment from registers 8 s .. 8 s + 7 of an fp32 MFMA result
+__device__ __forceinline__ bf16x8 regs_to_bf16(const f32x16& x, int s) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16(x[8 * s + 2 * i], x[8 * s + 2 * i + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------------------
+// prep: Dq = rowsum(dO * O) (fp32) and dq = 0
+// ---------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ out,
+                                                       const uint16_t* __restrict__ dout,
+                                                       long long rows, float* __restrict__ dvec,
+                                                       float* __restrict__ dq) {
+  constexpr int PER = D / 16;  // elements per lane (16 lanes per row)
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + li * PER;
+    float o[PER], g[PER];
+    if constexpr (OUT_F32) {
+#pragma unroll
+      for (int e = 0; e < PER; e += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>((const float*)out + base + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[e + u] = x[u];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; e += 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>((const uint16_t*)out + base + e);
+        o[e] = lo_bf16(w);
+        o[e + 1] = hi_bf16(w);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(dout + base + e);
+      g[e] = lo_bf16(w);
+      g[e + 1] = hi_bf16(w);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc = fmaf(o[e], g[e], acc);
+#pragma unroll
+    for (int e = 0; e < PER; e += 4)
+      *reinterpret_cast<f32x4*>(dq + base + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && li == 0) dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_kv: dK, dV of 128 keys (32 per wave) of one (head, KV block)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;   // k-steps over dims
+  constexpr int DT = D / 32;   // 32-dim tiles
+  constexpr int ROWB = D * 2;  // bytes of a query row in LDS
+  constexpr int TBYTES = kBwdQTile * ROWB;  // one query tile (Q or dO)
+  constexpr int LPR = ROWB / 16;            // lanes per row in a DMA instruction
+  constexpr int RPI = 64 / LPR;             // rows per DMA instruction
+  constexpr int NI = kBwdQTile / RPI;       // DMA instructions per tile and tensor
+  constexpr int NIW = NI / kBwdWaves;       // ... per wave
+  static_assert(NI % kBwdWaves == 0, "whole wave loads");
+  // buffer b: Q tile, dO tile, lse2 [32], Dq [32]
+  constexpr int BUF = 2 * TBYTES + 2 * kBwdQTile * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- which (head, block, key group); the groups of one block are
+  //      consecutive logical ids, hence on one XCD (they stream the same queries)
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kg = L % a.kgroups;
+  const int bk = L / a.kgroups;  // h * NB + gb
+  const int h = bk / a.NB;
+  const int gb = bk - h * a.NB;
+  const int sq = seq_of_block(a.cu_blocks, a.num_seqs, gb);
+  int seq_start, seq_len;
+  seq_span(a.cu_seqlens, sq, a.total_tokens, &seq_start, &seq_len);
+  const int blo = (gb - a.cu_blocks[sq]) * a.block_size;  // first key of the block (local)
+  const int bhi = min(blo + a.block_size, seq_len);
+  const int kwg = blo + kg * kBwdKeysPerWg;  // first key of the workgroup
+  if (kwg >= bhi) return;
+  const int kw = kwg + w * kBwdKeysPerWave;  // first key of the wave
+  const int key = kw + l32;                  // this lane's key (B column / C column)
+  const bool key_ok = key < bhi;
+
+  // ---- the wave's key rows: B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const size_t row = ((size_t)seq_start + min(key, bhi - 1)) * a.H + h;
+    const uint16_t* kp = a.k + row * D + 8 * hf;
+    const uint16_t* vp = a.v + row * D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
+      vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 16 * ks));
+    }
+  }
+
+  // ---- the query stream: historical list tiles, then own-block tiles
+  const int e0 = a.offsets[bk], e1 = a.offsets[bk + 1];
+  const int n_hist = (e1 - e0 + kBwdQTile - 1) / kBwdQTile;
+  const int own_q0 = kwg;  // queries before the group's first key attend none of its keys
+  const int n_own = (bhi - own_q0 + kBwdQTile - 1) / kBwdQTile;
+  const int ntiles = n_hist + n_own;
+
+  // per tile, lane `lane` of each DMA instruction fills row
+  // j * RPI + lane / LPR (instruction j = w + kBwdWaves * i), segment lane % LPR
+  const int lseg = lane % LPR;
+  auto row_token = [&](int t, int r, bool* valid) {
+    if (t < n_hist) {
+      const int e = e0 + t * kBwdQTile + r;
+      *valid = e < e1;
+      return (*valid ? a.list[e] : a.list[e0]) / a.topk;  // global token
+    }
+    const int p = own_q0 + (t - n_hist) * kBwdQTile + r;
+    *valid = p < bhi;
+    return seq_start + min(p, bhi - 1);
+  };
+  // issues the DMA of tile t's Q and dO rows into buffer b, and loads
+  // (into registers) the lse2 / Dq values of the rows this lane reports
+  float st_lse = 0.f, st_d = 0.f;
+  auto load_tile = [&](int t, int b) {
+    char* qd = smem + b * BUF;
+    char* od = qd + TBYTES;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int j = w + kBwdWaves * i;
+      const int r = j * RPI + lane / LPR;
+      bool valid;
+      const int tok = row_token(t, r, &valid);
+      const size_t src = (((size_t)tok * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
+      bwd_dma16((const char*)a.q + src, qd + j * 1024);
+      bwd_dma16((const char*)a.dout + src, od + j * 1024);
+    }
+    // lanes 0..31 of wave 0 report the 32 rows' softmax statistics
+    if (w == 0 && lane < kBwdQTile) {
+      bool valid;
+      const int tok = row_token(t, lane, &valid);
+      const size_t ri = (size_t)tok * a.H + h;
+      st_lse = valid ? a.lse[ri] * kLog2e : INFINITY;  // invalid row: P = 0
+      st_d = valid ? a.dvec[ri] : 0.f;
+    }
+  };
+  auto store_stats = [&](int b) {
+    if (w == 0 && lane < kBwdQTile) {
+      float* sl = (float*)(smem + b * BUF + 2 * TBYTES);
+      sl[lane] = st_lse;
+      sl[kBwdQTile + lane] = st_d;
+    }
+  };
+
+  // operand read offsets
+  const uint32_t rbase = (uint32_t)(l32 * ROWB + ((hf ^ bswz<ROWB>(l32)) << 4));
+  uint32_t tro[2][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    tro[0][dt] = tr_offset<ROWB>(lane, dt, 0);
+    tro[1][dt] = tr_offset<ROWB>(lane, dt, 1);
+  }
+
+  f32x16 dKT[DT], dVT[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dKT[dt][r] = 0.f; dVT[dt][r] = 0.f; }
+
+  if (ntiles > 0) {
+    load_tile(0, 0);
+    store_stats(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, b ^ 1);
+    const char* qt = smem + b * BUF;
+    const char* ot = qt + TBYTES;
+    const float* sl = (const float*)(qt + 2 * TBYTES);
+
+    f32x16 S, dP;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t o = rbase ^ (ks << 5);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + o);
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(ot + o);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dP, 0, 0, 0);
+    }
+    // S[r], dP[r]: query row 8 (r / 4) + 4 hf + r % 4 of the tile, key column l32
+    const bool own = t >= n_hist;
+    const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile;  // own tiles: local position of row 0
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * m + 4 * hf);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * m + u;
+        float p = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
+        if (own && key > qpos0 + 8 * m + 4 * hf + u) p = 0.f;
+        S[r] = p;
+        dP[r] = p * (dP[r] - d4[u]);
+      }
+    }
+    if (!key_ok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
+    }
+    const bf16x8 p0 = regs_to_bf16(S, 0), p1 = regs_to_bf16(S, 1);
+    const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ot, tro[0][dt], tro[1][dt]), p0,
+                                                        dVT[dt], 0, 0, 0);
+      dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          tr_frag(ot + 16 * ROWB, tro[0][dt], tro[1][dt]), p1, dVT[dt], 0, 0, 0);
+      dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qt, tro[0][dt], tro[1][dt]), s0,
+                                                        dKT[dt], 0, 0, 0);
+      dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          tr_frag(qt + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dKT[dt], 0, 0, 0);
+    }
+    if (t + 1 < ntiles) store_stats(b ^ 1);
+    __syncthreads();  // tile t + 1 has landed; buffer b is free again
+  }
+
+  // ---- dK = scale dK^T^T, dV = dV^T^T: lane = key, registers = dims
+  if (!key_ok) return;
+  const size_t orow = (((size_t)seq_start + key) * a.H + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d0 = 32 * dt + 8 * m + 4 * hf;
+      *reinterpret_cast<f32x4*>(a.dk + orow + d0) =
+          f32x4{dKT[dt][4 * m] * a.scale, dKT[dt][4 * m + 1] * a.scale,
+                dKT[dt][4 * m + 2] * a.scale, dKT[dt][4 * m + 3] * a.scale};
+      *reinterpret_cast<f32x4*>(a.dv + orow + d0) =
+          f32x4{dVT[dt][4 * m], dVT[dt][4 * m + 1], dVT[dt][4 * m + 2], dVT[dt][4 * m + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_q: dQ of one forward tile (4 waves x 32 queries) over its block's keys
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int CBYTES = kBwdChunk * ROWB;  // one K or V chunk
+  constexpr int NI = CBYTES / 1024;         // DMA instructions per chunk and tensor
+  constexpr int NIW = NI / kBwdWaves;
+  constexpr int RPI = 1024 / ROWB;          // rows per DMA instruction
+  static_assert(NI % kBwdWaves == 0, "whole wave loads");
+  constexpr int BUF = 2 * CBYTES;           // K chunk + V chunk
+  constexpr int TQ = kBwdWaves * 32;
+  constexpr int TS = D + 4;                 // floats per row of the final dQ staging
+  constexpr int SMEM = 2 * BUF > kBwdWaves * 32 * TS * 4 ? 2 * BUF : kBwdWaves * 32 * TS * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- tile decode (as the forward's historical / own tiles)
+  int h, seq_start, seq_len, key_lo, key_hi;
+  int qtok = -1, qpos = 0x7fffffff;
+  if (MODE == kBwdHist) {
+    const int4 ti = a.tile_info[blockIdx.x];
+    if (ti.x < 0) return;
+    h = ti.x / a.NB;
+    const int gb = ti.x - h * a.NB;
+    const int s = seq_of_block(a.cu_blocks, a.num_seqs, gb);
+    seq_span(a.cu_seqlens, s, a.total_tokens, &seq_start, &seq_len);
+    key_lo = (gb - a.cu_blocks[s]) * a.block_size;
+    key_hi = min(key_lo + a.block_size, seq_len);
+    const int j = ti.y + w * 32 + l32;
+    if (j < ti.z) qtok = a.list[j] / a.topk;
+  } else {
+    const int L = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+    const int bx = L % gridDim.x;
+    h = L / gridDim.x;
+    const int per_seq = a.tiles_per_unit * a.units_per_seq;
+    const int s = bx / per_seq;
+    const int rem = per_seq - 1 - (bx % per_seq);  // heavy tiles first
+    seq_span(a.cu_seqlens, s, a.total_tokens, &seq_start, &seq_len);
+    const int c = rem / a.tiles_per_unit;
+    const int sub = rem % a.tiles_per_unit;
+    key_lo = c * a.block_size;
+    const int q_lo = key_lo + sub * TQ;
+    const int q_hi = min(min(q_lo + TQ, key_lo + a.block_size), seq_len);
+    if (q_lo >= q_hi) return;
+    key_hi = q_hi;
+    const int p = q_lo + w * 32 + l32;
+    if (p < q_hi) { qtok = seq_start + p; qpos = p; }
+  }
+  const bool qv = qtok >= 0;
+  const size_t qrow = ((size_t)(qv ? qtok : seq_start) * a.H + h);
+  const float lse2 = qv ? a.lse[qrow] * kLog2e : INFINITY;  // invalid query: P = 0
+  const float dq_d = qv ? a.dvec[qrow] : 0.f;
+  bf16x8 qreg[KS], oreg[KS];
+  {
+    const uint16_t* qp = a.q + qrow * D + 8 * hf;
+    const uint16_t* op = a.dout + qrow * D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+      oreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
+    }
+  }
+  // smallest query position of the wave (own mode: chunks past it need the mask)
+  int wq_min = qv ? qpos : 0x7fffffff;
+  for (int o = 32; o >= 1; o >>= 1) wq_min = min(wq_min, __shfl_xor(wq_min, o));
+
+  // ---- K and V chunks of 64 keys; rows past the sequence end repeat its
+  //      last key (masked)
+  const int nchunks = (key_hi - key_lo + kBwdChunk - 1) / kBwdChunk;
+  const size_t hrow = (size_t)a.H * D * 2;  // bytes between consecutive tokens
+  const int lseg = lane % (ROWB / 16);
+  auto load_chunk = [&](int ch, int b) {
+    char* kd = smem + b * BUF;
+    char* vd = kd + CBYTES;
+    const int kp0 = key_lo + ch * kBwdChunk;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int j = w + kBwdWaves * i;
+      const int r = j * RPI + lane / (ROWB / 16);
+      const int kp = min(kp0 + r, seq_len - 1);
+      const size_t src = ((size_t)seq_start + kp) * hrow + (size_t)h * D * 2 +
+                         ((lseg ^ bswz<ROWB>(r)) << 4);
+      bwd_dma16((const char*)a.k + src, kd + j * 1024);
+      bwd_dma16((const char*)a.v + src, vd + j * 1024);
+    }
+  };
+
+  const uint32_t rbase = (uint32_t)(l32 * ROWB + ((hf ^ bswz<ROWB>(l32)) << 4));
+  uint32_t tro[2][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    tro[0][dt] = tr_offset<ROWB>(lane, dt, 0);
+    tro[1][dt] = tr_offset<ROWB>(lane, dt, 1);
+  }
+  f32x16 dQT[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dQT[dt][r] = 0.f;
+
+  load_chunk(0, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int b = ch & 1;
+    if (ch + 1 < nchunks) load_chunk(ch + 1, b ^ 1);
+    const char* kt = smem + b * BUF;
+    const char* vt = kt + CBYTES;
+    const int kp0 = key_lo + ch * kBwdChunk;
+#pragma unroll
+    for (int sc = 0; sc < 2; ++sc) {
+      f32x16 S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
+      const char* kr = kt + sc * 32 * ROWB;
+      const char* vr = vt + sc * 32 * ROWB;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t o = rbase ^ (ks << 5);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + o),
+                                                    qreg[ks], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vr + o),
+                                                     oreg[ks], dP, 0, 0, 0);
+      }
+      // S[r], dP[r]: key kp0 + 32 sc + 8 (r / 4) + 4 hf + r % 4, query column l32
+      const int kb = kp0 + 32 * sc + 4 * hf;
+      const bool need_mask = MODE != kBwdHist && kp0 + 32 * sc + 31 > wq_min;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -lse2));
+        if (need_mask && kb + 8 * (r >> 2) + (r & 3) > qpos) p = 0.f;
+        dP[r] = p * (dP[r] - dq_d);
+      }
+      const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dQT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(kr, tro[0][dt], tro[1][dt]),
+                                                          s0, dQT[dt], 0, 0, 0);
+        dQT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag(kr + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dQT[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // chunk ch + 1 has landed; buffer b is free again
+  }
+
+  // ---- dq += scale dQ: through LDS, so that each atomic instruction covers
+  //      one query row's consecutive dims
+  float* stg = (float*)smem + w * 32 * TS;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<f32x4*>(stg + l32 * TS + 32 * dt + 8 * m + 4 * hf) =
+          f32x4{dQT[dt][4 * m] * a.scale, dQT[dt][4 * m + 1] * a.scale,
+                dQT[dt][4 * m + 2] * a.scale, dQT[dt][4 * m + 3] * a.scale};
+  // the wave's own region only: a wave-level LDS fence suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int r = 0; r < 32; ++r) {
+    const int tok = __shfl(qtok, r);
+    if (tok < 0) continue;  // uniform: the same row for the whole wave
+    float* dst = a.dq + ((size_t)tok * a.H + h) * D;
+    for (int e = lane; e < D; e += 64) unsafeAtomicAdd(dst + e, stg[r * TS + e]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const Geo& g,
+                           float* dvec, float* dq, hipStream_t st) {
+  const long long rows = (long long)g.total_tokens * g.num_heads;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 15) / 16));
+#define MOBA_PREP(DD, F)                                                                     \
+  hipLaunchKernelGGL((bwd_prep_kernel<DD, F>), grid, dim3(256), 0, st, out, dout, rows, dvec, dq)
+  if (g.head_dim == 128) {
+    if (out_f32) MOBA_PREP(128, true); else MOBA_PREP(128, false);
+  } else {
+    if (out_f32) MOBA_PREP(64, true); else MOBA_PREP(64, false);
+  }
+#undef MOBA_PREP
+  return hipGetLastError();
+}
+
+static BwdArgs bwd_args(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                        int topk, float scale, const int32_t* list, const int32_t* offsets,
+                        const int4* tile_info, float* dq, float* dk, float* dv) {
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dvec = dvec;
+  a.cu_seqlens = g.cu_seqlens;
+  a.cu_blocks = g.cu_blocks;
+  a.num_seqs = g.num_seqs;
+  a.total_tokens = g.total_tokens;
+  a.H = g.num_heads;
+  a.block_size = g.block_size;
+  a.topk = topk;
+  a.NB = g.total_blocks;
+  a.scale = scale;
+  a.scale2 = scale * kLog2e;
+  a.list = list;
+  a.offsets = offsets;
+  a.tile_info = tile_info;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.kgroups = g.block_size / kBwdKeysPerWg + (g.block_size % kBwdKeysPerWg ? 1 : 0);
+  a.tiles_per_unit = (g.block_size + kBwdWaves * 32 - 1) / (kBwdWaves * 32);
+  a.units_per_seq = (g.max_seqlen + g.block_size - 1) / g.block_size;
+  return a;
+}
+
+hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                         int topk, float scale, const int32_t* list, const int32_t* offsets,
+                         float* dk, float* dv, hipStream_t st) {
+  if (g.total_blocks == 0) return hipSuccess;
+  const BwdArgs a = bwd_args(q, k, v, dout, lse, dvec, g, topk, scale, list, offsets, nullptr,
+                             nullptr, dk, dv);
+  const long long n = (long long)g.num_heads * g.total_blocks * a.kgroups;
+  dim3 grid((unsigned)n);
+  if (g.head_dim == 128)
+    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(64 * kBwdWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(64 * kBwdWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                        int topk, float scale, const int32_t* list, const int4* tile_info,
+                        long long hist_tiles, float* dq, hipStream_t st) {
+  if (g.total_tokens == 0) return hipSuccess;
+  const BwdArgs a = bwd_args(q, k, v, dout, lse, dvec, g, topk, scale, list, nullptr,
+                             tile_info, dq, nullptr, nullptr);
+  if (hist_tiles > 0) {
+    dim3 grid((unsigned)hist_tiles);
+    if (g.head_dim == 128)
+      hipLaunchKernelGGL((bwd_q_kernel<128, kBwdHist>), grid, dim3(64 * kBwdWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_q_kernel<64, kBwdHist>), grid, dim3(64 * kBwdWaves), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)(g.num_seqs * a.units_per_seq * a.tiles_per_unit), g.num_heads);
+  if (g.head_dim == 128)
+    hipLaunchKernelGGL((bwd_q_kernel<128, kBwdOwn>), grid, dim3(64 * kBwdWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<64, kBwdOwn>), grid, dim3(64 * kBwdWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -96,4 +96,18 @@ hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const 
                         bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
                         void* out, bool out_bf16, float* lse, hipStream_t st);
 
+// Backward: Dq = rowsum(dO * O) and dq = 0; dK, dV per (head, block, 128
+// keys) over the block's list and own-block queries; dQ over the forward's
+// historical tiles (tile_info) and own-block tiles, added to dq atomically.
+hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const Geo& g,
+                           float* dvec, float* dq, hipStream_t st);
+hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                         int topk, float scale, const int32_t* list, const int32_t* offsets,
+                         float* dk, float* dv, hipStream_t st);
+hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                        int topk, float scale, const int32_t* list, const int4* tile_info,
+                        long long hist_tiles, float* dq, hipStream_t st);
+
 }  // namespace moba

@@ -29,6 +29,7 @@ MOBA_BF16 = 1
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select", "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_attn_bwd_workspace_bytes", "moba_attn_bwd",
            "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
            "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
            "moba_profiler_names", "moba_profiler_destroy"]
@@ -76,6 +77,11 @@ def lib():
     L.moba_attn_workspace_bytes.argtypes = [i32] * 7
     L.moba_attn_fwd.restype = i32
     L.moba_attn_fwd.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, vp, sz, vp]
+    L.moba_attn_bwd_workspace_bytes.restype = sz
+    L.moba_attn_bwd_workspace_bytes.argtypes = [i32] * 7
+    L.moba_attn_bwd.restype = i32
+    L.moba_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32] + geo + [i32, vp, f32, vp, vp,
+                                                                          vp, vp, sz, vp]
     L.moba_dense_workspace_bytes.restype = sz
     L.moba_dense_workspace_bytes.argtypes = [i32] * 6
     L.moba_dense_causal_fwd.restype = i32
@@ -317,6 +323,27 @@ def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=N
     out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
                              workspace=workspace, stream=stream)
     return out, lse, idx
+
+
+def moba_attn_bwd(q, k, v, out, dout, lse, geom, topk, block_idx, scale, dq=None, dk=None,
+                  dv=None, workspace=None, stream=None):
+    """Gradients of moba_attn_fwd (fp32 dq, dk, dv) for the selections
+    block_idx; out and lse are the forward's outputs."""
+    H, d = _qkv_shape(q, geom)
+    shape = (geom.total_tokens, H, d)
+    dq = torch.empty(shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    nbytes = lib().moba_attn_bwd_workspace_bytes(_dtype_code(q.dtype), geom.total_tokens,
+                                                 geom.total_blocks, H, d, geom.block_size,
+                                                 int(topk))
+    if workspace is None:
+        workspace = _workspace(nbytes, q.device)
+    _check("moba_attn_bwd", lib().moba_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out.dtype), _ptr(dout), _ptr(lse),
+        _dtype_code(q.dtype), *geom.args(H, d), int(topk), _ptr(block_idx), float(scale),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
 
 
 def forward_minmax(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):

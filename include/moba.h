@@ -214,6 +214,42 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
                           float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Backward of moba_attn_fwd: gradients of out with respect to q, k and v for
+ * the selections in block_idx.  The block selection is a hard top-k and is
+ * not differentiated; gradients flow through the softmax attention over each
+ * query's selected tokens ("MoBA: Learned Block Sparsity for Long-Context
+ * Attention", "The Change": MoBA trains end to end as a drop-in for full
+ * attention; "MoBA: Mixture of Block Attention for Long-Context LLMs"
+ * (research.elamur.ai), "Key points").  With P[t, j] = exp(scale q_t.k_j -
+ * lse[t]) over the attended pairs and D[t] = dout[t] . out[t]:
+ *   dv[j] = sum_t P[t, j] dout[t]
+ *   dS[t, j] = P[t, j] (dout[t] . v[j] - D[t])
+ *   dq[t] = scale sum_j dS[t, j] k[j],   dk[j] = scale sum_t dS[t, j] q[t]
+ * (per head; sums over the attended pairs only).
+ *   q, k, v      the forward's inputs, bf16 only (MOBA_ERR_UNSUPPORTED else)
+ *   out, lse     the forward's outputs for the same inputs, selections and
+ *                scale (out in out_dtype, F32 or BF16; lse fp32)
+ *   dout         [total_tokens, num_heads, head_dim] bf16, upstream gradient
+ *   block_idx    the selections the forward used
+ *   dq, dk, dv   [total_tokens, num_heads, head_dim] fp32, written in full
+ *   workspace    at least moba_attn_bwd_workspace_bytes(...) bytes, 256-byte
+ *                aligned; contents on entry ignored
+ * dk and dv are deterministic; dq is summed with fp32 atomics over the
+ * query's (at most topk) selected blocks, so its last bits may vary between
+ * runs.
+ */
+size_t moba_attn_bwd_workspace_bytes(int dtype, int total_tokens, int total_blocks,
+                                     int num_heads, int head_dim, int block_size, int topk);
+
+moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                          int out_dtype, const void* dout, const float* lse, int dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                          int total_tokens, int max_seqlen, int total_blocks, int num_heads,
+                          int head_dim, int block_size, int topk, const int32_t* block_idx,
+                          float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Workspace bytes moba_dense_causal_fwd needs (0 when arguments are invalid). */
 size_t moba_dense_workspace_bytes(int dtype, int total_tokens, int total_blocks,
                                   int num_heads, int head_dim, int block_size);

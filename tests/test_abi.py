@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
