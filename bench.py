@@ -221,6 +221,49 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     return x, geom, ms_step, kern, dense_ms, rec_dense_stages
 
 
+def measure_bwd(torch, inputs, moba, w, dev, steps, warmup):
+    """Times `steps` backward passes (moba_attn_bwd: dq, dk, dv for one
+    upstream gradient) of one forward's selections, after `warmup`.  Returns
+    ms per step and per-stage HIP-event totals."""
+    print(f"[bench] workload {w.name}: backward", file=sys.stderr, flush=True)
+    x = inputs.make_inputs(w, device=dev)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    out, lse, idx = moba.forward(x["q"], x["k"], x["v"], geom, w.topk, w.scale)
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    dout = torch.empty_like(x["q"])
+    dout.copy_(torch.randn(x["q"].shape, generator=gen, device=dev, dtype=torch.float32))
+    torch.cuda.empty_cache()
+    H, d = w.heads, w.head_dim
+    dq, dk, dv = (torch.empty(x["q"].shape, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(moba.moba_attn_bwd_workspace_bytes(moba.MOBA_BF16, geom.total_tokens,
+                                                        geom.total_blocks, H, d, w.block_size,
+                                                        w.topk), dtype=torch.uint8, device=dev)
+
+    def step():
+        moba.moba_attn_bwd(x["q"], x["k"], x["v"], out, dout, lse, geom, w.topk, idx, w.scale,
+                           dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    prof = moba.Profiler().attach()
+    prof.reset()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = prof.summary()
+    prof.detach()
+    prof.close()
+    print(f"[bench] {w.name}: backward {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    del x, out, lse, idx, dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return ms, kern
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,10 +274,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--also", default="32k,10m,1m:minmax,1m:window,1m:sink1",
+    ap.add_argument("--also", default="32k,10m,1m:bwd,1m:minmax,1m:window,1m:sink1",
                     help="comma-separated extra workloads reported under other_workloads "
                          "(ms/layer, TFLOP/s, dense, speedup); NAME:minmax uses the min/max "
-                         "pooled gate, NAME:window or NAME:sinkN static routing; empty for none")
+                         "pooled gate, NAME:window or NAME:sinkN static routing, NAME:bwd the "
+                         "backward pass; empty for none")
     ap.add_argument("--also-steps", type=int, default=20,
                     help="timed steps of the extra workloads (3 above 256K tokens)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -329,6 +373,29 @@ def main():
         wname, _, gate = name.partition(":")
         gate = gate or "mean"
         wo = inputs.WORKLOADS[wname]
+        if gate == "bwd":
+            steps_b = min(args.also_steps, 3) if wo.total_tokens > (1 << 18) else args.also_steps
+            ms_b, kern_b = measure_bwd(torch, inputs, moba, wo, dev, steps_b, max(1, args.warmup))
+            pairs_b = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)[0]
+            d_b = wo.head_dim
+            st_b = {n: t / steps_b for n, (c, t) in kern_b.items()}
+            others[name] = {
+                "config": {"workload": wname, "pass": "backward (dq, dk, dv)",
+                           "seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": d_b,
+                           "block_size": wo.block_size, "topk": wo.topk},
+                "steps": steps_b,
+                "ms_per_layer": ms_b,
+                # algorithmic: 5 products of 2d flops per attended pair
+                "effective_tflops": 10.0 * d_b * pairs_b / (ms_b * 1e-3) / 1e12,
+                # issued: S and dP are formed in both kernels (7 products)
+                "issued_tflops": 14.0 * d_b * pairs_b / (ms_b * 1e-3) / 1e12,
+                "bwd_kv_tflops": (8.0 * d_b * pairs_b / (st_b["bwd_kv"] * 1e-3) / 1e12
+                                  if st_b.get("bwd_kv") else None),
+                "bwd_q_tflops": (6.0 * d_b * pairs_b / (st_b["bwd_q"] * 1e-3) / 1e12
+                                 if st_b.get("bwd_q") else None),
+                "stages_ms": st_b,
+            }
+            continue
         steps_o = args.also_steps if wo.total_tokens <= (1 << 18) else min(args.also_steps, 3)
         # gate variants of the headline workload reuse its dense time; above
         # 4M tokens the dense kernel (minutes) is not run: its time is

@@ -51,7 +51,7 @@ enum { kBwdHist = 0, kBwdOwn = 1 };
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerWave = 32;
 constexpr int kBwdKeysPerWg = kBwdWaves * kBwdKeysPerWave;  // 128
-constexpr int kBwdQTile = 32;                               // queries per bwd_kv step
+constexpr int kBwdQTile = 64;                               // queries per bwd_kv step
 constexpr int kBwdChunk = 64;                               // keys per bwd_q step
 
 struct BwdArgs {
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
   constexpr int NI = kBwdQTile / RPI;       // DMA instructions per tile and tensor
   constexpr int NIW = NI / kBwdWaves;       // ... per wave
   static_assert(NI % kBwdWaves == 0, "whole wave loads");
-  // buffer b: Q tile, dO tile, lse2 [32], Dq [32]
+  // buffer b: Q tile, dO tile, lse2 [64], Dq [64]
   constexpr int BUF = 2 * TBYTES + 2 * kBwdQTile * 4;
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
 
@@ -235,46 +235,52 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
   const int n_own = (bhi - own_q0 + kBwdQTile - 1) / kBwdQTile;
   const int ntiles = n_hist + n_own;
 
-  // per tile, lane `lane` of each DMA instruction fills row
-  // j * RPI + lane / LPR (instruction j = w + kBwdWaves * i), segment lane % LPR
+  // Per tile, lane `lane` of DMA instruction j = w + kBwdWaves i fills row
+  // j * RPI + lane / LPR, segment lane % LPR; lane `lane` of wave 0 reports
+  // row `lane`'s softmax statistics.  The rows' list entries are fetched two
+  // tiles ahead (raw values: the token is entry / topk), so no iteration
+  // waits on a list load before its DMA.
   const int lseg = lane % LPR;
-  auto row_token = [&](int t, int r, bool* valid) {
-    if (t < n_hist) {
-      const int e = e0 + t * kBwdQTile + r;
-      *valid = e < e1;
-      return (*valid ? a.list[e] : a.list[e0]) / a.topk;  // global token
-    }
-    const int p = own_q0 + (t - n_hist) * kBwdQTile + r;
-    *valid = p < bhi;
-    return seq_start + min(p, bhi - 1);
+  auto tile_row = [&](int t, int r) {  // raw value of row r of tile t
+    if (t < n_hist) return a.list[min(e0 + t * kBwdQTile + r, e1 - 1)];
+    return seq_start + min(own_q0 + (t - n_hist) * kBwdQTile + r, bhi - 1);
   };
-  // issues the DMA of tile t's Q and dO rows into buffer b, and loads
-  // (into registers) the lse2 / Dq values of the rows this lane reports
+  auto row_valid = [&](int t, int r) {
+    if (t < n_hist) return e0 + t * kBwdQTile + r < e1;
+    return own_q0 + (t - n_hist) * kBwdQTile + r < bhi;
+  };
+  auto to_token = [&](int t, int raw) { return t < n_hist ? raw / a.topk : raw; };
+  int raw_next[NIW + 1];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      raw_next[i] = tile_row(t, (w + kBwdWaves * i) * RPI + lane / LPR);
+    raw_next[NIW] = tile_row(t, lane);
+  };
+  // DMA of tile t's Q and dO rows into buffer b; wave 0 loads the rows'
+  // lse2 / Dq into registers (stored to LDS after this tile's compute)
   float st_lse = 0.f, st_d = 0.f;
-  auto load_tile = [&](int t, int b) {
+  auto issue_tile = [&](int t, int b) {
     char* qd = smem + b * BUF;
     char* od = qd + TBYTES;
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int j = w + kBwdWaves * i;
       const int r = j * RPI + lane / LPR;
-      bool valid;
-      const int tok = row_token(t, r, &valid);
+      const int tok = to_token(t, raw_next[i]);
       const size_t src = (((size_t)tok * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
       bwd_dma16((const char*)a.q + src, qd + j * 1024);
       bwd_dma16((const char*)a.dout + src, od + j * 1024);
     }
-    // lanes 0..31 of wave 0 report the 32 rows' softmax statistics
-    if (w == 0 && lane < kBwdQTile) {
-      bool valid;
-      const int tok = row_token(t, lane, &valid);
-      const size_t ri = (size_t)tok * a.H + h;
+    if (w == 0) {
+      const bool valid = row_valid(t, lane);
+      const size_t ri = (size_t)to_token(t, raw_next[NIW]) * a.H + h;
       st_lse = valid ? a.lse[ri] * kLog2e : INFINITY;  // invalid row: P = 0
       st_d = valid ? a.dvec[ri] : 0.f;
     }
   };
   auto store_stats = [&](int b) {
-    if (w == 0 && lane < kBwdQTile) {
+    if (w == 0) {
       float* sl = (float*)(smem + b * BUF + 2 * TBYTES);
       sl[lane] = st_lse;
       sl[kBwdQTile + lane] = st_d;
@@ -297,60 +303,70 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) { dKT[dt][r] = 0.f; dVT[dt][r] = 0.f; }
 
   if (ntiles > 0) {
-    load_tile(0, 0);
+    fetch(0);
+    issue_tile(0, 0);
     store_stats(0);
+    if (ntiles > 1) fetch(1);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int b = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1, b ^ 1);
+    if (t + 1 < ntiles) {
+      issue_tile(t + 1, b ^ 1);
+      if (t + 2 < ntiles) fetch(t + 2);
+    }
     const char* qt = smem + b * BUF;
     const char* ot = qt + TBYTES;
     const float* sl = (const float*)(qt + 2 * TBYTES);
-
-    f32x16 S, dP;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t o = rbase ^ (ks << 5);
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + o);
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(ot + o);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], S, 0, 0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dP, 0, 0, 0);
-    }
-    // S[r], dP[r]: query row 8 (r / 4) + 4 hf + r % 4 of the tile, key column l32
     const bool own = t >= n_hist;
     const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile;  // own tiles: local position of row 0
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * m + 4 * hf);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * m + u;
-        float p = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
-        if (own && key > qpos0 + 8 * m + 4 * hf + u) p = 0.f;
-        S[r] = p;
-        dP[r] = p * (dP[r] - d4[u]);
-      }
-    }
-    if (!key_ok) {
+    for (int hq = 0; hq < kBwdQTile / 32; ++hq) {  // 32-query halves of the tile
+      const char* qh = qt + hq * 32 * ROWB;
+      const char* oh = ot + hq * 32 * ROWB;
+      f32x16 S, dP;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
-    }
-    const bf16x8 p0 = regs_to_bf16(S, 0), p1 = regs_to_bf16(S, 1);
-    const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ot, tro[0][dt], tro[1][dt]), p0,
-                                                        dVT[dt], 0, 0, 0);
-      dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          tr_frag(ot + 16 * ROWB, tro[0][dt], tro[1][dt]), p1, dVT[dt], 0, 0, 0);
-      dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qt, tro[0][dt], tro[1][dt]), s0,
-                                                        dKT[dt], 0, 0, 0);
-      dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          tr_frag(qt + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dKT[dt], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t o = rbase ^ (ks << 5);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qh + o);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(oh + o);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dP, 0, 0, 0);
+      }
+      // S[r], dP[r]: query row 32 hq + 8 (r / 4) + 4 hf + r % 4 of the tile, key column l32
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * hq + 8 * m + 4 * hf);
+        const f32x4 d4 =
+            *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 32 * hq + 8 * m + 4 * hf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * m + u;
+          float p = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
+          if (own && key > qpos0 + 32 * hq + 8 * m + 4 * hf + u) p = 0.f;
+          S[r] = p;
+          dP[r] = p * (dP[r] - d4[u]);
+        }
+      }
+      if (!key_ok) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
+      }
+      const bf16x8 p0 = regs_to_bf16(S, 0), p1 = regs_to_bf16(S, 1);
+      const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(oh, tro[0][dt], tro[1][dt]),
+                                                          p0, dVT[dt], 0, 0, 0);
+        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag(oh + 16 * ROWB, tro[0][dt], tro[1][dt]), p1, dVT[dt], 0, 0, 0);
+        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qh, tro[0][dt], tro[1][dt]),
+                                                          s0, dKT[dt], 0, 0, 0);
+        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag(qh + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dKT[dt], 0, 0, 0);
+      }
     }
     if (t + 1 < ntiles) store_stats(b ^ 1);
     __syncthreads();  // tile t + 1 has landed; buffer b is free again

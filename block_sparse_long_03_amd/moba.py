@@ -227,6 +227,12 @@ def moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head
                                                head_dim, block_size, topk))
 
 
+def moba_attn_bwd_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
+                                  block_size, topk):
+    return int(lib().moba_attn_bwd_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
+                                                   head_dim, block_size, topk))
+
+
 def moba_dense_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
                                block_size):
     return int(lib().moba_dense_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
@@ -334,9 +340,8 @@ def moba_attn_bwd(q, k, v, out, dout, lse, geom, topk, block_idx, scale, dq=None
     dq = torch.empty(shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
-    nbytes = lib().moba_attn_bwd_workspace_bytes(_dtype_code(q.dtype), geom.total_tokens,
-                                                 geom.total_blocks, H, d, geom.block_size,
-                                                 int(topk))
+    nbytes = moba_attn_bwd_workspace_bytes(_dtype_code(q.dtype), geom.total_tokens,
+                                           geom.total_blocks, H, d, geom.block_size, int(topk))
     if workspace is None:
         workspace = _workspace(nbytes, q.device)
     _check("moba_attn_bwd", lib().moba_attn_bwd(
