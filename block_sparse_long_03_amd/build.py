@@ -33,10 +33,15 @@ CFLAGS = [
 ]
 
 
+# per-source code generation options: the backward kernels keep MFMA
+# operands and results in VGPRs (their register use fits without spills then)
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, build_dir=BUILD, defines=()):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = ([HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
-           + [f"-D{d}" for d in defines])
+           + SOURCE_FLAGS.get(src, []) + [f"-D{d}" for d in defines])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

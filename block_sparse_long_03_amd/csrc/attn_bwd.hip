@@ -36,6 +36,8 @@
 // in the MFMA row order 8(r/4) + 4(lane/32) + r%4) is used as the B operand
 // of the last ones directly: the A operand's k index follows the same order,
 // which the transpose read produces by picking the rows it gathers.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
   static_assert(NI % kBwdWaves == 0, "whole wave loads");
   // buffer b: Q tile, dO tile, lse2 [64], Dq [64]
   constexpr int BUF = 2 * TBYTES + 2 * kBwdQTile * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  constexpr int NBUF = 3;  // ring: tile t + 1 is resident while tile t is finished
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -302,74 +305,142 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dKT[dt][r] = 0.f; dVT[dt][r] = 0.f; }
 
+  // ---- software pipeline over 32-query halves (two per tile), scheduled by
+  // hand as in the forward kernel: in-order issue lets VALU work placed
+  // between MFMAs run while they are in the matrix pipe.  Step h:
+  //   A: S, dP of half h + 1 (16 MFMAs) with the softmax arithmetic of half h
+  //      (P = exp2(S scale log2e - lse log2e), causal mask, dS = P (dP - Dq))
+  //      and the LDS reads three MFMAs ahead;
+  //   B: dV^T += dO^T P and dK^T += Q^T dS of half h (16 MFMAs) with their
+  //      transpose reads three MFMAs ahead.
+  // Tile t lives in ring slot t % 3: its DMA is issued two tiles ahead, so
+  // the next tile's first half is resident during tile t's last step.
+  constexpr int PF = 3;
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto half_q = [&](int hh) { return (const char*)smem + ((hh >> 1) % NBUF) * BUF + (hh & 1) * 32 * ROWB; };
+  auto half_stats = [&](int hh) {
+    return (const float*)(smem + ((hh >> 1) % NBUF) * BUF + 2 * TBYTES) + 32 * (hh & 1);
+  };
+  auto opaque = [](uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  auto step = [&](int hh, f32x16& S, f32x16& dP, f32x16& SN, f32x16& dPN, auto more_t) {
+    constexpr bool MORE = decltype(more_t)::value;
+    const int t = hh >> 1;
+    const bool own = t >= n_hist;
+    const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile + 32 * (hh & 1);
+    const float* sl = half_stats(hh);
+    f32x4 l4, d4;  // statistics of rows 8 m + 4 hf .. + 3, read when m changes
+    const char* qn = MORE ? half_q(hh + 1) : half_q(hh);
+    const uint32_t rb = opaque(rbase);
+    bf16x8 qf[KS], df[KS];
+    if (MORE) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        qf[i] = *reinterpret_cast<const bf16x8*>(qn + (rb ^ (i << 5)));
+        df[i] = *reinterpret_cast<const bf16x8*>(qn + TBYTES + (rb ^ (i << 5)));
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { SN[r] = 0.f; dPN[r] = 0.f; }
+    }
+    // ---- A
+    constexpr int EA = 16 / KS;  // softmax values per k-step
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fence();
+      if (MORE) {
+        SN = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kreg[ks], SN, 0, 0, 0);
+        dPN = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[ks], vreg[ks], dPN, 0, 0, 0);
+        if (ks + PF < KS) {
+          qf[ks + PF] = *reinterpret_cast<const bf16x8*>(qn + (rb ^ ((ks + PF) << 5)));
+          df[ks + PF] = *reinterpret_cast<const bf16x8*>(qn + TBYTES + (rb ^ ((ks + PF) << 5)));
+        }
+      }
+#pragma unroll
+      for (int r = ks * EA; r < (ks + 1) * EA; ++r) {
+        const int m = r >> 2, u = r & 3;
+        if (u == 0) {
+          l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
+          d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * m + 4 * hf);
+        }
+        float pv = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
+        if (own && key > qpos0 + 8 * m + 4 * hf + u) pv = 0.f;
+        if (!key_ok) pv = 0.f;
+        S[r] = pv;
+        dP[r] = pv * (dP[r] - d4[u]);
+      }
+    }
+    fence();
+    // ---- B
+    const char* qh = half_q(hh);
+    const char* oh = qh + TBYTES;
+    bf16x8 pb[2], sb[2];
+    pb[0] = regs_to_bf16(S, 0);
+    pb[1] = regs_to_bf16(S, 1);
+    sb[0] = regs_to_bf16(dP, 0);
+    sb[1] = regs_to_bf16(dP, 1);
+    // MFMA i of B: dt = i / 4, kind = (i / 2) % 2 (dV, dK), s = i % 2
+    constexpr int NB = 4 * DT;
+    auto trf = [&](int i) {
+      const int dt = i >> 2, kind = (i >> 1) & 1, sidx = i & 1;
+      const char* base = (kind == 0 ? oh : qh) + sidx * 16 * ROWB;
+      return tr_frag(base, tro[0][dt], tro[1][dt]);
+    };
+    bf16x8 tf[NB];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) tf[i] = trf(i);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      fence();
+      const int dt = i >> 2, kind = (i >> 1) & 1, sidx = i & 1;
+      if (kind == 0)
+        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], pb[sidx], dVT[dt], 0, 0, 0);
+      else
+        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], sb[sidx], dKT[dt], 0, 0, 0);
+      if (i + PF < NB) tf[i + PF] = trf(i + PF);
+    }
+    fence();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
   if (ntiles > 0) {
     fetch(0);
     issue_tile(0, 0);
     store_stats(0);
-    if (ntiles > 1) fetch(1);
+    if (ntiles > 1) {
+      fetch(1);
+      issue_tile(1, 1);
+      store_stats(1);
+      if (ntiles > 2) fetch(2);
+    }
   }
   __syncthreads();
+  f32x16 S0, D0, S1, D1;
+  if (ntiles > 0) {  // S, dP of the first half
+    const char* q0 = half_q(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { S0[r] = 0.f; D0[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t o = rbase ^ (ks << 5);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q0 + o),
+                                                   kreg[ks], S0, 0, 0, 0);
+      D0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(q0 + TBYTES + o), vreg[ks], D0, 0, 0, 0);
+    }
+  }
   for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1, b ^ 1);
-      if (t + 2 < ntiles) fetch(t + 2);
+    if (t + 2 < ntiles) {
+      issue_tile(t + 2, (t + 2) % NBUF);
+      if (t + 3 < ntiles) fetch(t + 3);
     }
-    const char* qt = smem + b * BUF;
-    const char* ot = qt + TBYTES;
-    const float* sl = (const float*)(qt + 2 * TBYTES);
-    const bool own = t >= n_hist;
-    const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile;  // own tiles: local position of row 0
-#pragma unroll
-    for (int hq = 0; hq < kBwdQTile / 32; ++hq) {  // 32-query halves of the tile
-      const char* qh = qt + hq * 32 * ROWB;
-      const char* oh = ot + hq * 32 * ROWB;
-      f32x16 S, dP;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t o = rbase ^ (ks << 5);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qh + o);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(oh + o);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dP, 0, 0, 0);
-      }
-      // S[r], dP[r]: query row 32 hq + 8 (r / 4) + 4 hf + r % 4 of the tile, key column l32
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * hq + 8 * m + 4 * hf);
-        const f32x4 d4 =
-            *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 32 * hq + 8 * m + 4 * hf);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * m + u;
-          float p = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
-          if (own && key > qpos0 + 32 * hq + 8 * m + 4 * hf + u) p = 0.f;
-          S[r] = p;
-          dP[r] = p * (dP[r] - d4[u]);
-        }
-      }
-      if (!key_ok) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
-      }
-      const bf16x8 p0 = regs_to_bf16(S, 0), p1 = regs_to_bf16(S, 1);
-      const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(oh, tro[0][dt], tro[1][dt]),
-                                                          p0, dVT[dt], 0, 0, 0);
-        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_frag(oh + 16 * ROWB, tro[0][dt], tro[1][dt]), p1, dVT[dt], 0, 0, 0);
-        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qh, tro[0][dt], tro[1][dt]),
-                                                          s0, dKT[dt], 0, 0, 0);
-        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_frag(qh + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dKT[dt], 0, 0, 0);
-      }
-    }
-    if (t + 1 < ntiles) store_stats(b ^ 1);
-    __syncthreads();  // tile t + 1 has landed; buffer b is free again
+    step(2 * t, S0, D0, S1, D1, yes());
+    if (t + 1 < ntiles) step(2 * t + 1, S1, D1, S0, D0, yes());
+    else step(2 * t + 1, S1, D1, S0, D0, no());
+    if (t + 2 < ntiles) store_stats((t + 2) % NBUF);
+    __syncthreads();  // tile t + 2 has landed; slot t % 3 is free again
   }
 
   // ---- dK = scale dK^T^T, dV = dV^T^T: lane = key, registers = dims
