@@ -372,6 +372,72 @@ def attention_backward_masked(Q, K, V, dO, M, scale):
     return scale * dS @ K, scale * dS.T @ Q, dV
 
 
+def backward_dq_rows(Q, K, V, dO, cu_seqlens, block_size, idx, scale, rows):
+    """dQ of single (token, head) rows, from the row alone: with J the row's
+    attended tokens (step 4), p = softmax(scale K[J] q), o = p V[J],
+    dp = V[J] dO_t and ds = p * (dp - dO_t . o), dQ_t = scale ds K[J].
+    idx: [R, topk] selections of the rows.  Returns [R, d] fp64."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    out = np.zeros((len(rows), Q.shape[2]))
+    for r, (t, h) in enumerate(rows):
+        s, a, L = _seq_of_token(cu_seqlens, int(t))
+        J = attended_tokens(idx[r], int(t) - a, block_size)
+        q = np.asarray(Q[t, h], dtype=np.float64)
+        Kj = np.asarray(K[a + J, h], dtype=np.float64)
+        Vj = np.asarray(V[a + J, h], dtype=np.float64)
+        g = np.asarray(dO[t, h], dtype=np.float64)
+        x = scale * (Kj @ q)
+        p = np.exp(x - x.max())
+        p /= p.sum()
+        o = p @ Vj
+        ds = p * (Vj @ g - g @ o)
+        out[r] = scale * (ds @ Kj)
+    return out
+
+
+def backward_dkdv_keys(Q, K, V, dO, cu_seqlens, block_size, idx, scale, keys):
+    """dK, dV of single (key token, head) rows: the sums over every query t
+    that attends the key (the own-block queries at or after it, and the later
+    queries whose selection lists its block) of scale dS_tj q_t and P_tj dO_t,
+    each query's softmax taken over its own attended tokens.  idx [T, H, topk]
+    holds every row's selection.  Returns ([R, d], [R, d]) fp64."""
+    keys = np.asarray(keys, dtype=np.int64).reshape(-1, 2)
+    d = Q.shape[2]
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    rows_cache = {}
+
+    def row(t, h):  # (p over J, J, o) of query row (t, h)
+        if (t, h) not in rows_cache:
+            s, a, L = _seq_of_token(cu_seqlens, t)
+            J = attended_tokens(idx[t, h], t - a, block_size)
+            q = np.asarray(Q[t, h], dtype=np.float64)
+            x = scale * (np.asarray(K[a + J, h], dtype=np.float64) @ q)
+            p = np.exp(x - x.max())
+            p /= p.sum()
+            o = p @ np.asarray(V[a + J, h], dtype=np.float64)
+            rows_cache[(t, h)] = (p, a + J, o)
+        return rows_cache[(t, h)]
+
+    for r, (j, h) in enumerate(keys):
+        j, h = int(j), int(h)
+        s, a, L = _seq_of_token(cu_seqlens, j)
+        b = (j - a) // block_size
+        later = np.arange(a + (b + 1) * block_size, a + L)
+        sel = later[np.any(idx[later, h] == b, axis=1)] if len(later) else later
+        own = np.arange(j, min(a + (b + 1) * block_size, a + L))
+        kj = np.asarray(K[j, h], dtype=np.float64)
+        vj = np.asarray(V[j, h], dtype=np.float64)
+        for t in np.concatenate([own, sel]):
+            p, Jg, o = row(int(t), h)
+            ptj = p[np.searchsorted(Jg, j)]
+            g = np.asarray(dO[t, h], dtype=np.float64)
+            dstj = ptj * (g @ vj - g @ o)
+            dk[r] += scale * dstj * np.asarray(Q[t, h], dtype=np.float64)
+            dv[r] += ptj * g
+    return dk, dv
+
+
 def moba_backward_reference(Q, K, V, dO, cu_seqlens, block_size, idx, scale, heads=None):
     """dQ, dK, dV [T, H, d] fp64 of the attention over the given selections
     idx [T, H, topk] (the heads listed, default all; other heads are zero)."""

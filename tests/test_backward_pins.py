@@ -115,6 +115,33 @@ def test_gradient_identities():
     np.testing.assert_allclose(dv2, dv, atol=1e-12)
 
 
+def test_row_dq_matches_the_full_backward():
+    # the row-local dQ (used where the full backward is too large) against
+    # the full reference, which autograd and finite differences pin
+    cu = [0, 61, 61, 130]
+    T, H, d, B = 130, 2, 8, 8
+    q, k, v, do = _rand(T, H, d, 8)
+    idx = _selection(q, k, cu, B, 3)
+    dq, _, _ = mo.moba_backward_reference(q, k, v, do, cu, B, idx, 0.4)
+    rows = np.stack(np.meshgrid(np.arange(T), np.arange(H), indexing="ij"), -1).reshape(-1, 2)
+    got = mo.backward_dq_rows(q, k, v, do, cu, B, idx[rows[:, 0], rows[:, 1]], 0.4, rows)
+    np.testing.assert_allclose(got, dq[rows[:, 0], rows[:, 1]], atol=1e-12)
+
+
+def test_key_rows_match_the_full_backward():
+    # the key-local dK, dV (used at sizes where the full backward is too
+    # large) against the full reference
+    cu = [0, 61, 61, 130]
+    T, H, d, B = 130, 2, 8, 8
+    q, k, v, do = _rand(T, H, d, 9)
+    idx = _selection(q, k, cu, B, 3)
+    _, dk, dv = mo.moba_backward_reference(q, k, v, do, cu, B, idx, 0.4)
+    keys = np.stack(np.meshgrid(np.arange(T), np.arange(H), indexing="ij"), -1).reshape(-1, 2)
+    gk, gv = mo.backward_dkdv_keys(q, k, v, do, cu, B, idx, 0.4, keys)
+    np.testing.assert_allclose(gk, dk[keys[:, 0], keys[:, 1]], atol=1e-12)
+    np.testing.assert_allclose(gv, dv[keys[:, 0], keys[:, 1]], atol=1e-12)
+
+
 def test_token_mask_matches_brute_force_mask():
     cu = [0, 45]
     T, H, d, B = 45, 1, 4, 8
