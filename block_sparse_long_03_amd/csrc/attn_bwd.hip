@@ -79,13 +79,15 @@ struct BwdArgs {
 };
 
 // 16-byte segment swizzle of a tile row: rows of 256 B (d = 128) or 128 B
-// (d = 64).  A 16-row run of operand row reads and a transpose read (4
-// consecutive rows x 32 bytes per 16 lanes) both hit distinct banks.
+// (d = 64), 64 banks of 4 bytes.  A 16-lane pass of operand row reads (16
+// consecutive rows, one segment each) and a 32-lane pass of the transpose
+// read (4 consecutive rows x 4 consecutive segments) both hit distinct banks:
+// the 4 rows of a transpose pass land in different quarters of the banks.
 template <int ROWB>
 __device__ __forceinline__ int bswz(int row) {
-  if (ROWB == 256) return ((row & 7) << 1) | ((row >> 3) & 1);
+  if (ROWB == 256) return 4 * (row & 3) + ((row >> 2) & 3);
   const int m = (row >> 1) & 7;
-  return ((m & 3) << 1) | (m >> 2);
+  return 4 * (m & 1) + ((m >> 1) & 3);
 }
 
 __device__ __forceinline__ void bwd_dma16(const void* src, void* dst) {
