@@ -221,6 +221,40 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     return x, geom, ms_step, kern, dense_ms, rec_dense_stages
 
 
+def measured_peaks(torch, moba, dev):
+    """The rates this GPU sustains, to set next to the published peaks: the
+    library's bf16 MFMA probe (register operands only, two waves per SIMD)
+    and a plain 4 GiB device copy (read + write), each timed with events on
+    the current stream after a warmup."""
+    wg = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    moba.probe_mfma_rate(wg, 1000, sink)
+    iters = 1000000
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = moba.probe_mfma_rate(wg, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 3 * 2 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": mfma, "hbm_copy_gbps": copy,
+            "spec_mfma_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbps": PEAK_HBM_GBPS,
+            "method": f"moba_probe_mfma_rate: {wg} workgroups x 4 waves x 4 independent chains "
+                      f"x {iters} v_mfma_f32_32x32x16_bf16; copy: 3 x torch copy of 4 GiB fp32 "
+                      "(bytes read + written)"}
+
+
 def measure_bwd(torch, inputs, moba, w, dev, steps, warmup):
     """Times `steps` backward passes (moba_attn_bwd: dq, dk, dv for one
     upstream gradient) of one forward's selections, after `warmup`.  Returns
@@ -281,6 +315,8 @@ def main():
                          "backward pass; empty for none")
     ap.add_argument("--also-steps", type=int, default=20,
                     help="timed steps of the extra workloads (3 above 256K tokens)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA / copy rates reported next to the spec peaks")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -428,6 +464,11 @@ def main():
             "stages_ms": {n: t / steps_o for n, (c, t) in kern_o.items()},
         }
     rec["other_workloads"] = others
+    if not args.no_peaks:
+        print("[bench] measured peaks", file=sys.stderr, flush=True)
+        pk = measured_peaks(torch, moba, dev)
+        rec["measured_peaks"] = pk
+        rec["roofline"]["frac_of_measured_peak"] = rec["roofline"]["achieved"] / pk["mfma_bf16_tflops"]
     print(json.dumps(rec), flush=True)
 
 

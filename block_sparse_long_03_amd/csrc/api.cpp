@@ -476,6 +476,12 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
   return MOBA_OK;
 }
 
+moba_status moba_probe_mfma_rate(int workgroups, int iterations, float* sink, void* stream) {
+  if (workgroups < 1 || iterations < 1 || !sink) return MOBA_ERR_INVALID_ARG;
+  hipError_t e = moba::launch_mfma_rate(workgroups, iterations, sink, (hipStream_t)stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e);
+}
+
 size_t moba_dense_workspace_bytes(int dtype, int total_tokens, int total_blocks, int num_heads,
                                   int head_dim, int block_size) {
   if (!dtype_ok(dtype) || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||

@@ -110,4 +110,9 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int topk, float scale, const int32_t* list, const int4* tile_info,
                         long long hist_tiles, float* dq, hipStream_t st);
 
+// Measurement support: `workgroups` x 4 waves, each running 4 independent
+// chains of `iterations` 32x32x16 bf16 MFMAs (2 * 32 * 32 * 16 flops each);
+// sink holds workgroups * 256 floats.
+hipError_t launch_mfma_rate(int workgroups, int iterations, float* sink, hipStream_t st);
+
 }  // namespace moba

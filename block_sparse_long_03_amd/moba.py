@@ -28,11 +28,12 @@ MOBA_F32 = 0
 MOBA_BF16 = 1
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
-           "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select", "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
+           "moba_attn_workspace_bytes", "moba_attn_fwd",
            "moba_attn_bwd_workspace_bytes", "moba_attn_bwd",
            "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
            "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
-           "moba_profiler_names", "moba_profiler_destroy"]
+           "moba_profiler_names", "moba_profiler_destroy", "moba_probe_mfma_rate"]
 
 _lib = None
 
@@ -86,6 +87,8 @@ def lib():
     L.moba_dense_workspace_bytes.argtypes = [i32] * 6
     L.moba_dense_causal_fwd.restype = i32
     L.moba_dense_causal_fwd.argtypes = [vp, vp, vp, i32] + geo + [f32, vp, i32, vp, vp, sz, vp]
+    L.moba_probe_mfma_rate.restype = i32
+    L.moba_probe_mfma_rate.argtypes = [i32, i32, vp, vp]
     L.moba_profiler_create.restype = i32
     L.moba_profiler_create.argtypes = [ctypes.POINTER(vp)]
     L.moba_profiler_attach.restype = i32
@@ -402,3 +405,12 @@ def layer_forward(mode, q, k, v, geom, topk, scale, out_dtype=None, workspace=No
         return dense(q, k, v, geom, scale, out_dtype=out_dtype, workspace=workspace,
                      stream=stream)
     raise ValueError(f"unknown attention mode {mode!r}")
+
+
+def probe_mfma_rate(workgroups, iterations, sink, stream=None):
+    """Launches the bf16 MFMA rate probe (measurement support); sink: float32
+    device tensor of at least workgroups * 256 elements.  Returns its flop
+    count."""
+    _check("moba_probe_mfma_rate", lib().moba_probe_mfma_rate(
+        int(workgroups), int(iterations), _ptr(sink), _stream(stream)))
+    return workgroups * 4 * 4 * iterations * 2 * 32 * 32 * 16

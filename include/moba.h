@@ -289,6 +289,18 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
  *                          comma-separated list into buf (truncated to len)
  *   moba_profiler_destroy  frees p (detach it first)
  */
+/*
+ * Measurement support (not part of the computation): a sustained bf16 MFMA
+ * rate probe.  Launches `workgroups` workgroups of 4 waves; every wave runs
+ * 4 independent chains of `iterations` v_mfma_f32_32x32x16_bf16 on register
+ * operands (no memory traffic), i.e. workgroups * 4 * 4 * iterations * 32768
+ * flops.  The caller times it (events on `stream`) to obtain the rate the
+ * chip sustains at the clock it holds under full matrix load.
+ *   sink  device buffer of at least workgroups * 256 floats (written; the
+ *         values only keep the products from being optimised away)
+ */
+moba_status moba_probe_mfma_rate(int workgroups, int iterations, float* sink, void* stream);
+
 typedef struct moba_profiler moba_profiler;
 moba_status moba_profiler_create(moba_profiler** out);
 moba_status moba_profiler_attach(moba_profiler* p);

@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
@@ -119,6 +119,13 @@ def test_hybrid_schedule():
         moba.hybrid_schedule(4, 5)
     with pytest.raises(ValueError):
         moba.layer_forward("sparse", None, None, None, None, 3, 0.1)
+
+
+def test_probe_arguments(L):
+    E = moba.MOBA_ERR_INVALID_ARG
+    assert L.moba_probe_mfma_rate(0, 10, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 0, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 10, None, None) == E
 
 
 def test_unsupported(L):
