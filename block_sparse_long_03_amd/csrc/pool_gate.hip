@@ -671,18 +671,24 @@ __global__ __launch_bounds__(256) void static_select_kernel(
   seq_span(cu_seqlens, s, total_tokens, &start, &len);
   if (p0 >= len) return;
   const int n = min(kStaticTokens, len - p0);
-  const int hk = H * topk;
   const int sk = min(sink, topk - 1);
-  int32_t* out = block_idx + (size_t)(start + p0) * hk;
-  // consecutive threads write consecutive entries of the tile's rows
-  for (int e = threadIdx.x; e < n * hk; e += blockDim.x) {
-    const int tok = e / hk;
-    const int j = (e - tok * hk) % topk;
+  // one thread per (token, head) row; consecutive threads write consecutive rows
+  for (int r = threadIdx.x; r < n * H; r += blockDim.x) {
+    const int tok = r / H;
     const int c = (p0 + tok) / block_size;
-    int v;
-    if (c < topk) v = j <= c ? j : -1;
-    else v = j < sk ? j : c - (topk - 1 - sk) + (j - sk);
-    out[e] = v;
+    const int lo = c - (topk - 1 - sk);  // first recent block when c >= topk
+    int32_t* row = block_idx + ((size_t)(start + p0) * H + r) * topk;
+    auto value = [&](int j) {
+      if (c < topk) return j <= c ? j : -1;
+      return j < sk ? j : lo + (j - sk);
+    };
+    if ((topk & 3) == 0) {  // rows start 16-byte aligned
+      for (int j = 0; j < topk; j += 4)
+        *reinterpret_cast<int4*>(row + j) = make_int4(value(j), value(j + 1), value(j + 2),
+                                                      value(j + 3));
+    } else {
+      for (int j = 0; j < topk; ++j) row[j] = value(j);
+    }
   }
 }
 
