@@ -460,7 +460,8 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
     return hip_fail(e);
   if ((e = timed("bucket", s, [&] {
          return moba::launch_bucket(block_idx, g, topk, moba::kBwdTileQ, counts, offsets,
-                                    tile_offsets, list, tile_info, tiles, s);
+                                    tile_offsets, list, tile_info, tiles, s,
+                                    /*tokens_only=*/true);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = timed("bwd_kv", s, [&] {

@@ -70,7 +70,7 @@ struct BwdArgs {
   int units_per_seq;   // bwd_q own: max blocks per sequence
   int kgroups;         // bwd_kv: key groups per block (block_size / 128)
   float scale, scale2;  // softmax scale, scale * log2(e)
-  const int32_t* list;     // per (head, block) entries token * topk + slot
+  const int32_t* list;     // per (head, block) list of the global tokens that selected it
   const int32_t* offsets;  // list range of key h * NB + gb
   const int4* tile_info;   // bwd_q historical tiles
   float* dq;
@@ -99,9 +99,19 @@ __device__ __forceinline__ void bwd_dma16(const void* src, void* dst) {
 // it pairs with a B operand taken from an MFMA result's registers 8 s .. 8 s + 7.
 // off[0] / off[1] are the lane's byte offsets of its two 8-byte reads
 // relative to row R0 (a multiple of 16).
+//
+// The reads go through a restrict-qualified pointer.  The alias scope that
+// gives the read lets the compiler's wait insertion treat it like any other
+// LDS load; without it, every transpose read waits for all of the wave's LDS
+// DMA still in flight, i.e. for the prefetch of a later tile.  The kernels
+// order DMA and reads themselves: a tile is read only after the barrier that
+// follows the vmcnt(0) wait of the iteration that issued it.
+__device__ __forceinline__ s16x4 ds_read_tr(const lds_s16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 __device__ __forceinline__ bf16x8 tr_frag(const char* tile_r0, uint32_t off0, uint32_t off1) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile_r0 + off0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile_r0 + off1));
+  const s16x4 a = ds_read_tr((const lds_s16x4*)(tile_r0 + off0));
+  const s16x4 b = ds_read_tr((const lds_s16x4*)(tile_r0 + off1));
   const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, c);
 }
@@ -242,11 +252,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
 
   // Per tile, lane `lane` of DMA instruction j = w + kBwdWaves i fills row
   // j * RPI + lane / LPR, segment lane % LPR; lane `lane` of wave 0 reports
-  // row `lane`'s softmax statistics.  The rows' list entries are fetched two
-  // tiles ahead (raw values: the token is entry / topk), so no iteration
-  // waits on a list load before its DMA.
+  // row `lane`'s softmax statistics.  The rows' tokens are fetched two tiles
+  // ahead, so no iteration waits on a list load before its DMA.
   const int lseg = lane % LPR;
-  auto tile_row = [&](int t, int r) {  // raw value of row r of tile t
+  auto tile_row = [&](int t, int r) {  // global token of row r of tile t
     if (t < n_hist) return a.list[min(e0 + t * kBwdQTile + r, e1 - 1)];
     return seq_start + min(own_q0 + (t - n_hist) * kBwdQTile + r, bhi - 1);
   };
@@ -254,40 +263,40 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
     if (t < n_hist) return e0 + t * kBwdQTile + r < e1;
     return own_q0 + (t - n_hist) * kBwdQTile + r < bhi;
   };
-  auto to_token = [&](int t, int raw) { return t < n_hist ? raw / a.topk : raw; };
-  int raw_next[NIW + 1];
+  int tok_next[NIW + 1];
   auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      raw_next[i] = tile_row(t, (w + kBwdWaves * i) * RPI + lane / LPR);
-    raw_next[NIW] = tile_row(t, lane);
+      tok_next[i] = tile_row(t, (w + kBwdWaves * i) * RPI + lane / LPR);
+    tok_next[NIW] = tile_row(t, lane);
   };
-  // DMA of tile t's Q and dO rows into buffer b; wave 0 loads the rows'
-  // lse2 / Dq into registers (stored to LDS after this tile's compute)
+  // DMA of tile t's Q and dO rows into buffer b; wave 0 first loads the
+  // rows' lse / Dq into registers (stored to LDS after this tile's compute,
+  // so nothing waits on these loads, nor on the DMA issued after them, early)
   float st_lse = 0.f, st_d = 0.f;
   auto issue_tile = [&](int t, int b) {
+    if (w == 0) {
+      const bool valid = row_valid(t, lane);
+      const size_t ri = (size_t)tok_next[NIW] * a.H + h;
+      st_lse = valid ? a.lse[ri] : INFINITY;  // invalid row: P = 0 (scaled at store)
+      st_d = valid ? a.dvec[ri] : 0.f;
+    }
     char* qd = smem + b * BUF;
     char* od = qd + TBYTES;
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int j = w + kBwdWaves * i;
       const int r = j * RPI + lane / LPR;
-      const int tok = to_token(t, raw_next[i]);
+      const int tok = tok_next[i];
       const size_t src = (((size_t)tok * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
       bwd_dma16((const char*)a.q + src, qd + j * 1024);
       bwd_dma16((const char*)a.dout + src, od + j * 1024);
-    }
-    if (w == 0) {
-      const bool valid = row_valid(t, lane);
-      const size_t ri = (size_t)to_token(t, raw_next[NIW]) * a.H + h;
-      st_lse = valid ? a.lse[ri] * kLog2e : INFINITY;  // invalid row: P = 0
-      st_d = valid ? a.dvec[ri] : 0.f;
     }
   };
   auto store_stats = [&](int b) {
     if (w == 0) {
       float* sl = (float*)(smem + b * BUF + 2 * TBYTES);
-      sl[lane] = st_lse;
+      sl[lane] = st_lse * kLog2e;
       sl[kBwdQTile + lane] = st_d;
     }
   };
@@ -366,11 +375,21 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
           l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
           d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * m + 4 * hf);
         }
-        float pv = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
-        if (own && key > qpos0 + 8 * m + 4 * hf + u) pv = 0.f;
-        if (!key_ok) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
         S[r] = pv;
         dP[r] = pv * (dP[r] - d4[u]);
+      }
+    }
+    // Causal mask, only where a query of the half precedes a key of the wave
+    // (a wave-uniform test).  Keys past the block end need none: a lane's P
+    // and dS column feed only that lane's dK, dV column, which is not stored.
+    if (own && kw + kBwdKeysPerWave - 1 > qpos0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (key > qpos0 + 8 * (r >> 2) + 4 * hf + (r & 3)) {
+          S[r] = 0.f;
+          dP[r] = 0.f;
+        }
       }
     }
     fence();
@@ -499,7 +518,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
     key_lo = (gb - a.cu_blocks[s]) * a.block_size;
     key_hi = min(key_lo + a.block_size, seq_len);
     const int j = ti.y + w * 32 + l32;
-    if (j < ti.z) qtok = a.list[j] / a.topk;
+    if (j < ti.z) qtok = a.list[j];
   } else {
     const int L = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
     const int bx = L % gridDim.x;

@@ -20,12 +20,14 @@ constexpr int kBucketLdsBins = 8192;  // LDS histogram limit (heads x past block
 // block_idx, read in memory order (consecutive lanes take consecutive rows,
 // so a wave reads one contiguous range), counted into an LDS histogram per
 // (head, past block) and flushed with one global atomic per touched bin.
-// The scatter pass reserves a range per bin, then places each entry.
+// The scatter pass reserves a range per bin, then places each entry: the
+// global token times slot_stride plus its slot, or (slot_stride 0) the token
+// alone.
 template <bool kScatter>
 __global__ __launch_bounds__(256) void bucket_pass_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int tile_tokens,
-    int H, int NB, int block_size, int topk, int32_t* __restrict__ counts,
+    int H, int NB, int block_size, int topk, int slot_stride, int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ list) {
   __shared__ int32_t hist[kBucketLdsBins];
   __shared__ int32_t basev[kScatter ? kBucketLdsBins : 1];
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
     for (int r = threadIdx.x; r < nrows; r += 256)
       walk(r, [&](int h, int e, int slot, int p) {
         const size_t key = (size_t)h * NB + gb0 + e;
-        list[offsets[key] + atomicAdd(&counts[key], 1)] = (start + p) * topk + slot;
+        list[offsets[key] + atomicAdd(&counts[key], 1)] = slot_stride ? (start + p) * slot_stride + slot : start + p;
       });
     return;
   }
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
   for (int r = threadIdx.x; r < nrows; r += 256)
     walk(r, [&](int h, int e, int slot, int p) {
       const int b = h * nbins + e;
-      list[basev[b] + atomicAdd(&hist[b], 1)] = (start + p) * topk + slot;
+      list[basev[b] + atomicAdd(&hist[b], 1)] = slot_stride ? (start + p) * slot_stride + slot : start + p;
     });
 }
 
@@ -175,7 +177,9 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
 
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st) {
+                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st,
+                         bool tokens_only) {
+  const int slot_stride = tokens_only ? 0 : topk;
   const int n = g.num_heads * g.total_blocks;
   if (n > 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
@@ -189,13 +193,13 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<false>), grid, dim3(256), 0, st, block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.total_blocks, g.block_size, topk, counts, offsets, list);
+                       g.total_blocks, g.block_size, topk, slot_stride, counts, offsets, list);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, st, counts, n, tile_q,
                      offsets, tile_offsets);
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<true>), grid, dim3(256), 0, st, block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.total_blocks, g.block_size, topk, counts, offsets, list);
+                       g.total_blocks, g.block_size, topk, slot_stride, counts, offsets, list);
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
                        st, offsets, tile_offsets, n, tile_q, max_tiles, tile_info);

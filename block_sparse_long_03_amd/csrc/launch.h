@@ -56,9 +56,11 @@ hipError_t launch_static_select(const Geo& g, int topk, int sink, int32_t* block
 // of tiles, and the scatter of (token, slot) entries into per-block lists.
 // With tile_info, also writes {key, first entry, end entry, 0} for each of
 // the max_tiles tiles of tile_q rows (key -1 past the last tile).
+// List entries are token * topk + slot, or (tokens_only) the global token.
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st);
+                         int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st,
+                         bool tokens_only = false);
 
 // Transposed, key-permuted fp16 copy of V per (block, head) for the MFMA
 // kernels, scaled per head by 2^-e (vmax_bits[h] receives max |v|).
