@@ -132,6 +132,28 @@ __device__ __forceinline__ uint32_t tr_offset(int lane, int dt, int second) {
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
+// acc += A B with the accumulator pinned to AGPRs.  The dK^T / dV^T sums of
+// the key-centric kernel live there for the whole query stream, which leaves
+// the VGPRs to the stream's operands and scores; left to the register
+// allocator, the two register files trade whole 16-register accumulators
+// every step.  The compiler sees an opaque instruction here, so the MFMA
+// hazards are covered by hand: `settle` (issued before the accumulators are
+// read by anything else) waits out the last MFMA's write, and the VGPR
+// operands written by VALU code are five wait states old when first read.
+__device__ __forceinline__ void mfma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_agpr_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void zero_agpr(f32x16& acc) {
+  const bf16x8 z = {};
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+__device__ __forceinline__ void settle(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
 // bf16 B fragment from registers 8 s .. 8 s + 7 of an fp32 MFMA result
 __device__ __forceinline__ bf16x8 regs_to_bf16(const f32x16& x, int s) {
   u32x4 w;
@@ -312,9 +334,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
 
   f32x16 dKT[DT], dVT[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dKT[dt][r] = 0.f; dVT[dt][r] = 0.f; }
+  for (int dt = 0; dt < DT; ++dt) {
+    zero_agpr(dKT[dt]);
+    zero_agpr(dVT[dt]);
+  }
 
   // ---- software pipeline over 32-query halves (two per tile), scheduled by
   // hand as in the forward kernel: in-order issue lets VALU work placed
@@ -415,10 +438,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
     for (int i = 0; i < NB; ++i) {
       fence();
       const int dt = i >> 2, kind = (i >> 1) & 1, sidx = i & 1;
-      if (kind == 0)
-        dVT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], pb[sidx], dVT[dt], 0, 0, 0);
+      if (i == 0)
+        mfma_acc_agpr_first(dVT[dt], tf[i], pb[sidx]);
+      else if (kind == 0)
+        mfma_acc_agpr(dVT[dt], tf[i], pb[sidx]);
       else
-        dKT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], sb[sidx], dKT[dt], 0, 0, 0);
+        mfma_acc_agpr(dKT[dt], tf[i], sb[sidx]);
       if (i + PF < NB) tf[i + PF] = trf(i + PF);
     }
     fence();
@@ -458,13 +483,19 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
       if (t + 3 < ntiles) fetch(t + 3);
     }
     step(2 * t, S0, D0, S1, D1, yes());
-    if (t + 1 < ntiles) step(2 * t + 1, S1, D1, S0, D0, yes());
-    else step(2 * t + 1, S1, D1, S0, D0, no());
+    // after the last tile, the A part reads a free slot and its scores go
+    // unused: one path through the loop keeps the accumulators in place
+    step(2 * t + 1, S1, D1, S0, D0, yes());
     if (t + 2 < ntiles) store_stats((t + 2) % NBUF);
     __syncthreads();  // tile t + 2 has landed; slot t % 3 is free again
   }
 
   // ---- dK = scale dK^T^T, dV = dV^T^T: lane = key, registers = dims
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    settle(dKT[dt]);
+    settle(dVT[dt]);
+  }
   if (!key_ok) return;
   const size_t orow = (((size_t)seq_start + key) * a.H + h) * D;
 #pragma unroll
