@@ -46,7 +46,6 @@ namespace moba {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void_b;
 
 enum { kBwdHist = 0, kBwdOwn = 1 };
 
@@ -90,8 +89,15 @@ __device__ __forceinline__ int bswz(int row) {
   return 4 * (m & 1) + ((m >> 1) & 3);
 }
 
-__device__ __forceinline__ void bwd_dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_b*)dst, 16, 0, 0);
+
+// 16 bytes per lane from a per-lane global address into LDS (dst + 16 lane).
+// The rows of a query-list tile are arbitrary tokens, whose offsets from any
+// one base can exceed the 32-bit reach of the buffer form; this form takes a
+// full address per lane, at the price of coarser LDS waits while it is in
+// flight (see lds_dma16).
+typedef __attribute__((address_space(3))) void lds_flat_t;
+__device__ __forceinline__ void lds_dma16_flat(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_flat_t*)dst, 16, 0, 0);
 }
 
 // A operand X^T (dims 32 dt .. + 31 as rows, 16 tile rows R0 .. R0 + 15 as k)
@@ -311,8 +317,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
       const int r = j * RPI + lane / LPR;
       const int tok = tok_next[i];
       const size_t src = (((size_t)tok * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
-      bwd_dma16((const char*)a.q + src, qd + j * 1024);
-      bwd_dma16((const char*)a.dout + src, od + j * 1024);
+      lds_dma16_flat((const char*)a.q + src, qd + j * 1024);
+      lds_dma16_flat((const char*)a.dout + src, od + j * 1024);
     }
   };
   auto store_stats = [&](int b) {
@@ -589,21 +595,23 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
   // ---- K and V chunks of 64 keys; rows past the sequence end repeat its
   //      last key (masked)
   const int nchunks = (key_hi - key_lo + kBwdChunk - 1) / kBwdChunk;
-  const size_t hrow = (size_t)a.H * D * 2;  // bytes between consecutive tokens
   const int lseg = lane % (ROWB / 16);
   auto load_chunk = [&](int ch, int b) {
     char* kd = smem + b * BUF;
     char* vd = kd + CBYTES;
     const int kp0 = key_lo + ch * kBwdChunk;
+    const size_t row0 = (((size_t)seq_start + kp0) * a.H + h) * D * 2;
+    const char* kbase = (const char*)a.k + row0;
+    const char* vbase = (const char*)a.v + row0;
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int j = w + kBwdWaves * i;
       const int r = j * RPI + lane / (ROWB / 16);
-      const int kp = min(kp0 + r, seq_len - 1);
-      const size_t src = ((size_t)seq_start + kp) * hrow + (size_t)h * D * 2 +
-                         ((lseg ^ bswz<ROWB>(r)) << 4);
-      bwd_dma16((const char*)a.k + src, kd + j * 1024);
-      bwd_dma16((const char*)a.v + src, vd + j * 1024);
+      // 16-byte unit of the row's segment relative to the chunk's first key
+      const int kr = min(kp0 + r, seq_len - 1) - kp0;
+      const uint32_t unit = (uint32_t)(kr * a.H) * (D / 8) + (lseg ^ bswz<ROWB>(r));
+      lds_dma16(kbase, unit, kd + j * 1024);
+      lds_dma16(vbase, unit, vd + j * 1024);
     }
   };
 

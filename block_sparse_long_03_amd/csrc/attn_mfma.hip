@@ -22,8 +22,8 @@
 // operands are single 16-byte LDS reads.
 //
 // K and V^T chunks of 64 keys are double-buffered in LDS and filled by direct
-// global-to-LDS loads (global_load_lds_dwordx4: each wave instruction writes
-// 1 KiB of consecutive LDS, no registers involved) while the previous chunk
+// global-to-LDS loads (buffer_load_dwordx4 ... lds: each wave instruction
+// writes 1 KiB of consecutive LDS, no registers involved) while the previous chunk
 // is computed; one barrier per chunk.  The LDS tiles are unpadded and
 // XOR-swizzled in 16-byte segments so that the MFMA operand reads are free of
 // bank conflicts: rows of 256 B use segment ^ (row & 15), rows of 128 B use
@@ -75,13 +75,6 @@ __device__ __forceinline__ int swz(int row) {
   return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from global memory straight into LDS: lane i's data lands
-// at dst + 16 i (dst is wave-uniform)
-__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
 // Lazy rescaling: the running max used as the exponent base only moves when a
 // new score exceeds it by more than 2^8, so the O accumulators are rescaled
 // rarely; probabilities stay below 256 (exact in the final normalisation).
@@ -211,7 +204,7 @@ void attn_mfma_kernel(MfmaArgs a) {
       for (int i = 0; i < KIW; ++i) {
         const int j = w + kWaves * i;
         if (NKI % kWaves == 0 || j < NKI)
-          lds_dma16(kb + (size_t)i * KROWS_I * krow_bytes + koff0, kl + j * 1024);
+          lds_dma16(kb + (size_t)i * KROWS_I * krow_bytes, koff0 >> 4, kl + j * 1024);
       }
     } else {
 #pragma unroll
@@ -219,7 +212,8 @@ void attn_mfma_kernel(MfmaArgs a) {
         const int j = w + kWaves * i;
         const int over = max(0, kp0 + krow0 + i * KROWS_I - (seq_len - 1));
         if (NKI % kWaves == 0 || j < NKI)
-          lds_dma16(kb + (size_t)(i * KROWS_I - over) * krow_bytes + koff0, kl + j * 1024);
+          lds_dma16(kb, (uint32_t)(((size_t)(i * KROWS_I - over) * krow_bytes + koff0) >> 4),
+                    kl + j * 1024);
       }
     }
   };
@@ -235,7 +229,7 @@ void attn_mfma_kernel(MfmaArgs a) {
     for (int i = 0; i < VIW; ++i) {
       const int j = w + kWaves * i;
       if (NVI % kWaves == 0 || j < NVI)
-        lds_dma16(vb + (size_t)i * VROWS_I * a.block_size * 2 + voff0, vl + j * 1024);
+        lds_dma16(vb + (size_t)i * VROWS_I * a.block_size * 2, voff0 >> 4, vl + j * 1024);
     }
     off_next += kTK;
     if (off_next == a.block_size) { off_next = 0; ++gb_next; }

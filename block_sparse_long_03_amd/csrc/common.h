@@ -37,6 +37,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// Global -> LDS DMA, 16 bytes per lane: lane l's bytes come from
+// base + 16 unit and land at dst + 16 l (base and dst wave-uniform; 16 unit
+// below 4 GiB: the buffer offset arithmetic is 32-bit).  This is the buffer
+// (MUBUF) form of the load with a 16-byte record stride.  The global (FLAT)
+// form takes a full address per lane, but the compiler's wait bookkeeping
+// counts a FLAT load to LDS as possibly touching LDS through the scalar-and-
+// LDS counter too; while one is in flight it then waits for every LDS read
+// outstanding (lgkmcnt(0)) before any LDS operand is used, which flattens the
+// operand prefetch of the MFMA loops.
+constexpr int kBufferWord3 = 0x00020000;  // 32-bit raw data format, gfx9 family
+typedef __attribute__((address_space(3))) void lds_dma_t;
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t unit, void* dst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 16, -1, kBufferWord3);
+  __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (lds_dma_t*)dst, 16, unit, 0, 0, 0, 0);
+}
+
 // fp16 <-> fp32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
