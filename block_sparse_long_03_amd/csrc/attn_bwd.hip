@@ -11,12 +11,12 @@
 //
 // Three kernels:
 //   bwd_prep:  Dq = rowsum(dO * O) per (token, head) and dq = 0.
-//   bwd_kv:    KV-centric.  A workgroup owns 32 keys per wave of one (head,
-//              KV block) and streams every query that attends them: the
-//              block's historical list (queries that selected it), then the
-//              own-block queries at or after its first key (causal mask).
-//              dK and dV stay in registers for the whole stream and are
-//              written once: no atomics, deterministic.
+//   bwd_kv:    KV-centric.  A workgroup owns 128 keys of one (head, KV
+//              block), 32 per pair of waves, and streams every query that
+//              attends them: the block's historical list (queries that
+//              selected it), then the own-block queries at or after its
+//              first key (causal mask).  dK and dV stay in registers for the
+//              whole stream and are written once: no atomics, deterministic.
 //   bwd_q:     the forward's tiles (a (head, block) list tile of gathered
 //              queries, or an own-block query tile) against the block's keys
 //              in 64-key chunks; each wave keeps its 32 queries' dQ in
@@ -24,7 +24,7 @@
 //              coalesced atomics (a query gets at most topk additions).
 //
 // Products:
-//   bwd_kv:  S = Q K^T and dP = dO V^T (A = query rows from LDS, B = the
+//   bwd_kv:  S = Q K^T and dP = dO V^T (A = query rows from LDS, B = a
 //            wave's key rows in registers), then dV^T += dO^T P and
 //            dK^T += Q^T dS, whose A operands (dims x queries) come from the
 //            row-major query tiles through the LDS transpose read
@@ -51,7 +51,7 @@ enum { kBwdHist = 0, kBwdOwn = 1 };
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerWave = 32;
-constexpr int kBwdKeysPerWg = kBwdWaves * kBwdKeysPerWave;  // 128
+constexpr int kBwdKeysPerWg = 4 * kBwdKeysPerWave;  // bwd_kv: 4 wave pairs x 32 keys
 constexpr int kBwdQTile = 64;                               // queries per bwd_kv step
 constexpr int kBwdChunk = 64;                               // keys per bwd_q step
 
@@ -216,10 +216,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_kv: dK, dV of 128 keys (32 per wave) of one (head, KV block)
+// bwd_kv, paired waves: dK, dV of 128 keys of one (head, KV block) with 8
+// waves.  Waves w and w + 4 share the keys 32 (w % 4) .. + 31 and split the
+// work of each 32-query half: wave w (the P wave) forms S = Q K^T, P and
+// dV^T += dO^T P; wave w + 4 (the dS wave) forms dP = dO V^T, takes P
+// through LDS, and accumulates dK^T += Q^T dS with dS = P (dP - Dq).  Each
+// wave holds one key-row operand (K or V) and one 64-register accumulator,
+// which brings it to two waves per SIMD; the two waves of a pair sit on one
+// SIMD (wave ids w and w + 4), so one's softmax arithmetic runs beside the
+// other's products.
 // ---------------------------------------------------------------------------
+constexpr int kBwdPairWaves = 8;
+
+constexpr int kListSlots = 4;  // list slices of four tiles in LDS
+
+// 4 bytes per lane from a per-lane global address into LDS (dst + 4 lane)
+__device__ __forceinline__ void lds_dma4_flat(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_flat_t*)dst, 4, 0, 0);
+}
+
+// Workgroup barrier that leaves the wave's newest n vector-memory loads in
+// flight (all of them LDS DMA, whose data no wave reads before a later
+// barrier) and completes everything older; the LDS accesses of the wave are
+// complete too.  n is wave-uniform and at most 8.
+__device__ __forceinline__ void tile_barrier(int n) {
+  switch (n) {
+#define MOBA_TB(N) \
+    case N: asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    MOBA_TB(1) MOBA_TB(2) MOBA_TB(3) MOBA_TB(4) MOBA_TB(5) MOBA_TB(6) MOBA_TB(7) MOBA_TB(8)
+#undef MOBA_TB
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
+
+// LDS handoff between the waves of a workgroup: the wave's own LDS accesses
+// are complete, then the barrier.  Unlike __syncthreads it does not wait for
+// vector memory, so the DMA of later tiles stays in flight; the asm's memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs a) {
   constexpr int KS = D / 16;   // k-steps over dims
   constexpr int DT = D / 32;   // 32-dim tiles
   constexpr int ROWB = D * 2;  // bytes of a query row in LDS
@@ -227,21 +266,23 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
   constexpr int LPR = ROWB / 16;            // lanes per row in a DMA instruction
   constexpr int RPI = 64 / LPR;             // rows per DMA instruction
   constexpr int NI = kBwdQTile / RPI;       // DMA instructions per tile and tensor
-  constexpr int NIW = NI / kBwdWaves;       // ... per wave
-  static_assert(NI % kBwdWaves == 0, "whole wave loads");
+  constexpr int NIW = NI / kBwdPairWaves;   // ... per wave
+  static_assert(NI % kBwdPairWaves == 0, "whole wave loads");
   // buffer b: Q tile, dO tile, lse2 [64], Dq [64]
   constexpr int BUF = 2 * TBYTES + 2 * kBwdQTile * 4;
-  constexpr int NBUF = 3;  // ring: tile t + 1 is resident while tile t is finished
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
+  constexpr int NBUF = 3;
+  constexpr int XBYTES = 64 * 16 * 4;  // one 32 x 32 fp32 tile of P, C layout
+  __shared__ __attribute__((aligned(1024)))
+  char smem[NBUF * BUF + 4 * 2 * XBYTES + kListSlots * kBwdQTile * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = w & 3;           // pair: keys 32 pw .. of the workgroup
+  const bool pwave = w < 4;       // the P wave of the pair (else the dS wave)
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- which (head, block, key group); the groups of one block are
-  //      consecutive logical ids, hence on one XCD (they stream the same queries)
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int kg = L % a.kgroups;
   const int bk = L / a.kgroups;  // h * NB + gb
@@ -250,86 +291,76 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
   const int sq = seq_of_block(a.cu_blocks, a.num_seqs, gb);
   int seq_start, seq_len;
   seq_span(a.cu_seqlens, sq, a.total_tokens, &seq_start, &seq_len);
-  const int blo = (gb - a.cu_blocks[sq]) * a.block_size;  // first key of the block (local)
+  const int blo = (gb - a.cu_blocks[sq]) * a.block_size;
   const int bhi = min(blo + a.block_size, seq_len);
-  const int kwg = blo + kg * kBwdKeysPerWg;  // first key of the workgroup
+  const int kwg = blo + kg * kBwdKeysPerWg;
   if (kwg >= bhi) return;
-  const int kw = kwg + w * kBwdKeysPerWave;  // first key of the wave
-  const int key = kw + l32;                  // this lane's key (B column / C column)
+  const int kw = kwg + pw * kBwdKeysPerWave;
+  const int key = kw + l32;
   const bool key_ok = key < bhi;
 
-  // ---- the wave's key rows: B operands of S = Q K^T and dP = dO V^T
-  bf16x8 kreg[KS], vreg[KS];
+  // ---- the wave's key rows: K (P wave) or V (dS wave), B operand of its product
+  bf16x8 brow[KS];
   {
     const size_t row = ((size_t)seq_start + min(key, bhi - 1)) * a.H + h;
-    const uint16_t* kp = a.k + row * D + 8 * hf;
-    const uint16_t* vp = a.v + row * D + 8 * hf;
+    const uint16_t* bp = (pwave ? a.k : a.v) + row * D + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
-      vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 16 * ks));
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      brow[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bp + 16 * ks));
   }
 
-  // ---- the query stream: historical list tiles, then own-block tiles
+  // ---- the query stream: historical list tiles, then own-block tiles.
+  // Everything a tile needs reaches LDS by DMA (list entries, Q and dO rows,
+  // lse and Dq), and no register waits on a vector-memory load inside the
+  // loop, so the barrier that ends iteration t waits only for what earlier
+  // iterations issued: the list slice of tile x is loaded at iteration x - 4,
+  // its rows and statistics at iteration x - 2, and it is read at iteration x.
   const int e0 = a.offsets[bk], e1 = a.offsets[bk + 1];
   const int n_hist = (e1 - e0 + kBwdQTile - 1) / kBwdQTile;
-  const int own_q0 = kwg;  // queries before the group's first key attend none of its keys
+  const int own_q0 = kwg;
   const int n_own = (bhi - own_q0 + kBwdQTile - 1) / kBwdQTile;
   const int ntiles = n_hist + n_own;
-
-  // Per tile, lane `lane` of DMA instruction j = w + kBwdWaves i fills row
-  // j * RPI + lane / LPR, segment lane % LPR; lane `lane` of wave 0 reports
-  // row `lane`'s softmax statistics.  The rows' tokens are fetched two tiles
-  // ahead, so no iteration waits on a list load before its DMA.
   const int lseg = lane % LPR;
-  auto tile_row = [&](int t, int r) {  // global token of row r of tile t
-    if (t < n_hist) return a.list[min(e0 + t * kBwdQTile + r, e1 - 1)];
+  int32_t* lring = (int32_t*)(smem + NBUF * BUF + 4 * 2 * XBYTES);  // kListSlots x 64
+  auto rows_of = [&](int t) {  // valid rows of tile t
+    return t < n_hist ? min(kBwdQTile, e1 - e0 - t * kBwdQTile)
+                      : min(kBwdQTile, bhi - own_q0 - (t - n_hist) * kBwdQTile);
+  };
+  // global token of row r of tile t (rows past the end repeat the last one)
+  auto tile_row = [&](int t, int r) {
+    if (t < n_hist) return lring[(t % kListSlots) * kBwdQTile + min(r, rows_of(t) - 1)];
     return seq_start + min(own_q0 + (t - n_hist) * kBwdQTile + r, bhi - 1);
   };
-  auto row_valid = [&](int t, int r) {
-    if (t < n_hist) return e0 + t * kBwdQTile + r < e1;
-    return own_q0 + (t - n_hist) * kBwdQTile + r < bhi;
+  auto issue_list = [&](int t) {  // wave 1: list entries of historical tile t
+    const int j = min(e0 + t * kBwdQTile + lane, e1 - 1);
+    lds_dma4_flat(a.list + j, lring + (t % kListSlots) * kBwdQTile);
   };
-  int tok_next[NIW + 1];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      tok_next[i] = tile_row(t, (w + kBwdWaves * i) * RPI + lane / LPR);
-    tok_next[NIW] = tile_row(t, lane);
-  };
-  // DMA of tile t's Q and dO rows into buffer b; wave 0 first loads the
-  // rows' lse / Dq into registers (stored to LDS after this tile's compute,
-  // so nothing waits on these loads, nor on the DMA issued after them, early)
-  float st_lse = 0.f, st_d = 0.f;
   auto issue_tile = [&](int t, int b) {
-    if (w == 0) {
-      const bool valid = row_valid(t, lane);
-      const size_t ri = (size_t)tok_next[NIW] * a.H + h;
-      st_lse = valid ? a.lse[ri] : INFINITY;  // invalid row: P = 0 (scaled at store)
-      st_d = valid ? a.dvec[ri] : 0.f;
-    }
     char* qd = smem + b * BUF;
     char* od = qd + TBYTES;
+    if (w == 0) {
+      const size_t ri = (size_t)tile_row(t, lane) * a.H + h;
+      float* sl = (float*)(qd + 2 * TBYTES);
+      lds_dma4_flat(a.lse + ri, sl);
+      lds_dma4_flat(a.dvec + ri, sl + kBwdQTile);
+    }
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
-      const int j = w + kBwdWaves * i;
+      const int j = w + kBwdPairWaves * i;
       const int r = j * RPI + lane / LPR;
-      const int tok = tok_next[i];
-      const size_t src = (((size_t)tok * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
+      const size_t src = (((size_t)tile_row(t, r) * a.H + h) * D) * 2 + ((lseg ^ bswz<ROWB>(r)) << 4);
       lds_dma16_flat((const char*)a.q + src, qd + j * 1024);
       lds_dma16_flat((const char*)a.dout + src, od + j * 1024);
     }
   };
-  auto store_stats = [&](int b) {
-    if (w == 0) {
-      float* sl = (float*)(smem + b * BUF + 2 * TBYTES);
-      sl[lane] = st_lse * kLog2e;
-      sl[kBwdQTile + lane] = st_d;
-    }
+  // vector-memory instructions this wave issues in iteration t
+  auto issued_in = [&](int t) {
+    int n = 0;
+    if (t + 2 < ntiles) n += 2 * NIW + (w == 0 ? 2 : 0);
+    if (w == 1 && t + 4 < n_hist) n += 1;
+    return n;
   };
 
-  // operand read offsets
   const uint32_t rbase = (uint32_t)(l32 * ROWB + ((hf ^ bswz<ROWB>(l32)) << 4));
   uint32_t tro[2][DT];
 #pragma unroll
@@ -337,105 +368,92 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
     tro[0][dt] = tr_offset<ROWB>(lane, dt, 0);
     tro[1][dt] = tr_offset<ROWB>(lane, dt, 1);
   }
-
-  f32x16 dKT[DT], dVT[DT];
+  f32x16 acc[DT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    zero_agpr(dKT[dt]);
-    zero_agpr(dVT[dt]);
-  }
+  for (int dt = 0; dt < DT; ++dt) zero_agpr(acc[dt]);
 
-  // ---- software pipeline over 32-query halves (two per tile), scheduled by
-  // hand as in the forward kernel: in-order issue lets VALU work placed
-  // between MFMAs run while they are in the matrix pipe.  Step h:
-  //   A: S, dP of half h + 1 (16 MFMAs) with the softmax arithmetic of half h
-  //      (P = exp2(S scale log2e - lse log2e), causal mask, dS = P (dP - Dq))
-  //      and the LDS reads three MFMAs ahead;
-  //   B: dV^T += dO^T P and dK^T += Q^T dS of half h (16 MFMAs) with their
-  //      transpose reads three MFMAs ahead.
-  // Tile t lives in ring slot t % 3: its DMA is issued two tiles ahead, so
-  // the next tile's first half is resident during tile t's last step.
   constexpr int PF = 3;
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  auto half_q = [&](int hh) { return (const char*)smem + ((hh >> 1) % NBUF) * BUF + (hh & 1) * 32 * ROWB; };
-  auto half_stats = [&](int hh) {
-    return (const float*)(smem + ((hh >> 1) % NBUF) * BUF + 2 * TBYTES) + 32 * (hh & 1);
-  };
   auto opaque = [](uint32_t x) {
     asm volatile("" : "+v"(x));
     return x;
   };
-  auto step = [&](int hh, f32x16& S, f32x16& dP, f32x16& SN, f32x16& dPN, auto more_t) {
-    constexpr bool MORE = decltype(more_t)::value;
+  // P of the pair's current half, C layout: register chunk c of lane l at
+  // 16 bytes x (64 c + l), so that each 16-lane pass of a store or load
+  // covers 256 consecutive bytes
+  float* xb0 = (float*)(smem + NBUF * BUF + pw * 2 * XBYTES);
+
+  auto step = [&](int hh) {
     const int t = hh >> 1;
-    const bool own = t >= n_hist;
-    const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile + 32 * (hh & 1);
-    const float* sl = half_stats(hh);
-    f32x4 l4, d4;  // statistics of rows 8 m + 4 hf .. + 3, read when m changes
-    const char* qn = MORE ? half_q(hh + 1) : half_q(hh);
+    const char* tile = (const char*)smem + (t % NBUF) * BUF;
+    const char* half = tile + (hh & 1) * 32 * ROWB;
+    const float* sl = (const float*)(tile + 2 * TBYTES) + 32 * (hh & 1);
+    float* xb = xb0 + (hh & 1) * (XBYTES / 4);
+    // ---- S = Q K^T (P wave) or dP = dO V^T (dS wave)
+    const char* an = half + (pwave ? 0 : TBYTES);
     const uint32_t rb = opaque(rbase);
-    bf16x8 qf[KS], df[KS];
-    if (MORE) {
+    bf16x8 af[KS];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) {
-        qf[i] = *reinterpret_cast<const bf16x8*>(qn + (rb ^ (i << 5)));
-        df[i] = *reinterpret_cast<const bf16x8*>(qn + TBYTES + (rb ^ (i << 5)));
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { SN[r] = 0.f; dPN[r] = 0.f; }
-    }
-    // ---- A
-    constexpr int EA = 16 / KS;  // softmax values per k-step
+    for (int i = 0; i < PF; ++i) af[i] = *reinterpret_cast<const bf16x8*>(an + (rb ^ (i << 5)));
+    f32x16 X;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       fence();
-      if (MORE) {
-        SN = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kreg[ks], SN, 0, 0, 0);
-        dPN = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[ks], vreg[ks], dPN, 0, 0, 0);
-        if (ks + PF < KS) {
-          qf[ks + PF] = *reinterpret_cast<const bf16x8*>(qn + (rb ^ ((ks + PF) << 5)));
-          df[ks + PF] = *reinterpret_cast<const bf16x8*>(qn + TBYTES + (rb ^ ((ks + PF) << 5)));
-        }
+      if (ks == 0) {
+        const f32x16 z = {};
+        X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], brow[0], z, 0, 0, 0);
+      } else {
+        X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], brow[ks], X, 0, 0, 0);
       }
-#pragma unroll
-      for (int r = ks * EA; r < (ks + 1) * EA; ++r) {
-        const int m = r >> 2, u = r & 3;
-        if (u == 0) {
-          l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
-          d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * m + 4 * hf);
-        }
-        const float pv = __builtin_amdgcn_exp2f(fmaf(S[r], a.scale2, -l4[u]));
-        S[r] = pv;
-        dP[r] = pv * (dP[r] - d4[u]);
-      }
-    }
-    // Causal mask, only where a query of the half precedes a key of the wave
-    // (a wave-uniform test).  Keys past the block end need none: a lane's P
-    // and dS column feed only that lane's dK, dV column, which is not stored.
-    if (own && kw + kBwdKeysPerWave - 1 > qpos0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (key > qpos0 + 8 * (r >> 2) + 4 * hf + (r & 3)) {
-          S[r] = 0.f;
-          dP[r] = 0.f;
-        }
-      }
+      if (ks + PF < KS) af[ks + PF] = *reinterpret_cast<const bf16x8*>(an + (rb ^ ((ks + PF) << 5)));
     }
     fence();
-    // ---- B
-    const char* qh = half_q(hh);
-    const char* oh = qh + TBYTES;
-    bf16x8 pb[2], sb[2];
-    pb[0] = regs_to_bf16(S, 0);
-    pb[1] = regs_to_bf16(S, 1);
-    sb[0] = regs_to_bf16(dP, 0);
-    sb[1] = regs_to_bf16(dP, 1);
-    // MFMA i of B: dt = i / 4, kind = (i / 2) % 2 (dV, dK), s = i % 2
-    constexpr int NB = 4 * DT;
+    if (pwave) {
+      // P = exp2(S scale log2e - lse log2e), the masks, then P to the pair
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          X[4 * m + u] = __builtin_amdgcn_exp2f(fmaf(X[4 * m + u], a.scale2, -l4[u] * kLog2e));
+      }
+      // rows past the tile's end repeat its last row: P = 0 there
+      const int vrows = rows_of(t) - 32 * (hh & 1);
+      if (vrows < 32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * hf + (r & 3) >= vrows) X[r] = 0.f;
+      }
+      const bool own = t >= n_hist;
+      const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile + 32 * (hh & 1);
+      if (own && kw + kBwdKeysPerWave - 1 > qpos0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key > qpos0 + 8 * (r >> 2) + 4 * hf + (r & 3)) X[r] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4*>(xb + 4 * (64 * c + lane)) =
+            f32x4{X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]};
+    }
+    lds_barrier();  // P of this half is in LDS
+    if (!pwave) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(xb + 4 * (64 * c + lane));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * c + 4 * hf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) X[4 * c + u] = p4[u] * (X[4 * c + u] - d4[u]);
+      }
+    }
+    // ---- dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave)
+    const char* tb = half + (pwave ? TBYTES : 0);
+    bf16x8 xb16[2];
+    xb16[0] = regs_to_bf16(X, 0);
+    xb16[1] = regs_to_bf16(X, 1);
+    constexpr int NB = 2 * DT;  // MFMA i: dt = i / 2, s = i % 2
     auto trf = [&](int i) {
-      const int dt = i >> 2, kind = (i >> 1) & 1, sidx = i & 1;
-      const char* base = (kind == 0 ? oh : qh) + sidx * 16 * ROWB;
-      return tr_frag(base, tro[0][dt], tro[1][dt]);
+      return tr_frag(tb + (i & 1) * 16 * ROWB, tro[0][i >> 1], tro[1][i >> 1]);
     };
     bf16x8 tf[NB];
 #pragma unroll
@@ -443,77 +461,45 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       fence();
-      const int dt = i >> 2, kind = (i >> 1) & 1, sidx = i & 1;
       if (i == 0)
-        mfma_acc_agpr_first(dVT[dt], tf[i], pb[sidx]);
-      else if (kind == 0)
-        mfma_acc_agpr(dVT[dt], tf[i], pb[sidx]);
+        mfma_acc_agpr_first(acc[0], tf[0], xb16[0]);
       else
-        mfma_acc_agpr(dKT[dt], tf[i], sb[sidx]);
+        mfma_acc_agpr(acc[i >> 1], tf[i], xb16[i & 1]);
       if (i + PF < NB) tf[i + PF] = trf(i + PF);
     }
     fence();
   };
-  using yes = std::integral_constant<bool, true>;
-  using no = std::integral_constant<bool, false>;
 
-  if (ntiles > 0) {
-    fetch(0);
-    issue_tile(0, 0);
-    store_stats(0);
-    if (ntiles > 1) {
-      fetch(1);
-      issue_tile(1, 1);
-      store_stats(1);
-      if (ntiles > 2) fetch(2);
-    }
-  }
-  __syncthreads();
-  f32x16 S0, D0, S1, D1;
-  if (ntiles > 0) {  // S, dP of the first half
-    const char* q0 = half_q(0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { S0[r] = 0.f; D0[r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t o = rbase ^ (ks << 5);
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q0 + o),
-                                                   kreg[ks], S0, 0, 0, 0);
-      D0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(q0 + TBYTES + o), vreg[ks], D0, 0, 0, 0);
-    }
-  }
+  if (w == 1)
+    for (int x = 0; x < 4 && x < n_hist; ++x) issue_list(x);
+  __syncthreads();  // list slices of tiles 0 - 3
+  for (int x = 0; x < 2 && x < ntiles; ++x) issue_tile(x, x);
+  __syncthreads();  // tiles 0 and 1
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) {
-      issue_tile(t + 2, (t + 2) % NBUF);
-      if (t + 3 < ntiles) fetch(t + 3);
-    }
-    step(2 * t, S0, D0, S1, D1, yes());
-    // after the last tile, the A part reads a free slot and its scores go
-    // unused: one path through the loop keeps the accumulators in place
-    step(2 * t + 1, S1, D1, S0, D0, yes());
-    if (t + 2 < ntiles) store_stats((t + 2) % NBUF);
-    __syncthreads();  // tile t + 2 has landed; slot t % 3 is free again
+    // every wave is past tile t - 1: its slot takes tile t + 2
+    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NBUF);
+    if (w == 1 && t + 4 < n_hist) issue_list(t + 4);
+    step(2 * t);
+    step(2 * t + 1);
+    // everything issued before this iteration has landed (tile t + 1, the
+    // list slice of tile t + 3); this iteration's loads stay in flight
+    tile_barrier(issued_in(t));
   }
 
-  // ---- dK = scale dK^T^T, dV = dV^T^T: lane = key, registers = dims
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    settle(dKT[dt]);
-    settle(dVT[dt]);
-  }
+  for (int dt = 0; dt < DT; ++dt) settle(acc[dt]);
   if (!key_ok) return;
   const size_t orow = (((size_t)seq_start + key) * a.H + h) * D;
+  float* dst = pwave ? a.dv : a.dk;
+  const float sc = pwave ? 1.f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int d0 = 32 * dt + 8 * m + 4 * hf;
-      *reinterpret_cast<f32x4*>(a.dk + orow + d0) =
-          f32x4{dKT[dt][4 * m] * a.scale, dKT[dt][4 * m + 1] * a.scale,
-                dKT[dt][4 * m + 2] * a.scale, dKT[dt][4 * m + 3] * a.scale};
-      *reinterpret_cast<f32x4*>(a.dv + orow + d0) =
-          f32x4{dVT[dt][4 * m], dVT[dt][4 * m + 1], dVT[dt][4 * m + 2], dVT[dt][4 * m + 3]};
+      *reinterpret_cast<f32x4*>(dst + orow + d0) =
+          f32x4{acc[dt][4 * m] * sc, acc[dt][4 * m + 1] * sc, acc[dt][4 * m + 2] * sc,
+                acc[dt][4 * m + 3] * sc};
     }
 }
 
@@ -756,9 +742,9 @@ hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v
   const long long n = (long long)g.num_heads * g.total_blocks * a.kgroups;
   dim3 grid((unsigned)n);
   if (g.head_dim == 128)
-    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(64 * kBwdWaves), 0, st, a);
+    hipLaunchKernelGGL(bwd_kv_pair_kernel<128>, grid, dim3(64 * kBwdPairWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(64 * kBwdWaves), 0, st, a);
+    hipLaunchKernelGGL(bwd_kv_pair_kernel<64>, grid, dim3(64 * kBwdPairWaves), 0, st, a);
   return hipGetLastError();
 }
 
