@@ -365,6 +365,9 @@ def main():
                 "avg_launch_ms": avg_h, "flops_per_launch": hist_flops}
     n_o, ms_o = kern.get("attn_own", (0, 0.0))
     own_tflops = 4.0 * d * own_p / (ms_o / max(n_o, 1) * 1e-3) / 1e12 if ms_o > 0 else None
+    # both attention kernels together: 4d flops per attended pair over their summed time
+    t_attn = avg_h + (ms_o / max(n_o, 1) if ms_o > 0 else 0.0)
+    attn_frac = (flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if t_attn > 0 else None
     n_p, ms_p = kern.get("pool_keys", (0, 0.0))
     pool_bytes = geom.total_tokens * H * d * q.element_size() + geom.total_blocks * H * d * 4
     pool_gbps = pool_bytes / (ms_p / max(n_p, 1) * 1e-3) / 1e9 if ms_p > 0 else None
@@ -394,6 +397,7 @@ def main():
         "stages": stages,
         "dense_stages": {n: {"launches": c, "ms": t} for n, (c, t) in rec_dense_stages.items()},
         "own_block_tflops": own_tflops,
+        "attention_mfma_frac": attn_frac,
         "pool_gbps": pool_gbps,
         "pool_hbm_frac": pool_gbps / PEAK_HBM_GBPS if pool_gbps else None,
         "roofline": roofline,
