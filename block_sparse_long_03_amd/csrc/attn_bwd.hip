@@ -268,12 +268,21 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
   constexpr int NI = kBwdQTile / RPI;       // DMA instructions per tile and tensor
   constexpr int NIW = NI / kBwdPairWaves;   // ... per wave
   static_assert(NI % kBwdPairWaves == 0, "whole wave loads");
-  // buffer b: Q tile, dO tile, lse2 [64], Dq [64]
-  constexpr int BUF = 2 * TBYTES + 2 * kBwdQTile * 4;
-  constexpr int NBUF = 3;
-  constexpr int XBYTES = 64 * 16 * 4;  // one 32 x 32 fp32 tile of P, C layout
-  __shared__ __attribute__((aligned(1024)))
-  char smem[NBUF * BUF + 4 * 2 * XBYTES + kListSlots * kBwdQTile * 4];
+  constexpr int NBUF = 3;                   // tile slots
+  constexpr int SBYTES = 2 * kBwdQTile * 4; // lse and Dq of one tile
+  constexpr int XBYTES = 64 * 16 * 4;       // one 32 x 32 fp32 tile of P, C layout
+  // LDS: Q ring | dO ring | statistics ring | P exchange | list ring.  Every
+  // operand read adds a per-lane register offset (which holds the ring's
+  // start) to a compile-time slot and half offset below 64 KiB, which the
+  // LDS instruction carries as its immediate: no address arithmetic per read.
+  constexpr int Q_OFF = 0;
+  constexpr int O_OFF = NBUF * TBYTES;
+  constexpr int S_OFF = 2 * NBUF * TBYTES;
+  constexpr int X_OFF = S_OFF + NBUF * SBYTES;
+  constexpr int L_OFF = X_OFF + 4 * 2 * XBYTES;
+  constexpr int LDS_BYTES = L_OFF + kListSlots * kBwdQTile * 4;
+  static_assert((NBUF - 1) * TBYTES + 48 * ROWB < 65536, "immediate offsets");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
   const int n_own = (bhi - own_q0 + kBwdQTile - 1) / kBwdQTile;
   const int ntiles = n_hist + n_own;
   const int lseg = lane % LPR;
-  int32_t* lring = (int32_t*)(smem + NBUF * BUF + 4 * 2 * XBYTES);  // kListSlots x 64
+  int32_t* lring = (int32_t*)(smem + L_OFF);  // kListSlots x 64 entries
   auto rows_of = [&](int t) {  // valid rows of tile t
     return t < n_hist ? min(kBwdQTile, e1 - e0 - t * kBwdQTile)
                       : min(kBwdQTile, bhi - own_q0 - (t - n_hist) * kBwdQTile);
@@ -335,12 +344,13 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
     const int j = min(e0 + t * kBwdQTile + lane, e1 - 1);
     lds_dma4_flat(a.list + j, lring + (t % kListSlots) * kBwdQTile);
   };
-  auto issue_tile = [&](int t, int b) {
-    char* qd = smem + b * BUF;
-    char* od = qd + TBYTES;
+  auto issue_tile = [&](int t, auto slot_t) {
+    constexpr int SLOT = decltype(slot_t)::value;
+    char* qd = smem + Q_OFF + SLOT * TBYTES;
+    char* od = smem + O_OFF + SLOT * TBYTES;
     if (w == 0) {
       const size_t ri = (size_t)tile_row(t, lane) * a.H + h;
-      float* sl = (float*)(qd + 2 * TBYTES);
+      float* sl = (float*)(smem + S_OFF + SLOT * SBYTES);
       lds_dma4_flat(a.lse + ri, sl);
       lds_dma4_flat(a.dvec + ri, sl + kBwdQTile);
     }
@@ -361,40 +371,44 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
     return n;
   };
 
+  // ---- per-lane LDS offsets, computed once and kept in registers (the asm
+  // keeps the compiler from folding them back into per-read arithmetic)
+  auto opaque = [](uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   const uint32_t rbase = (uint32_t)(l32 * ROWB + ((hf ^ bswz<ROWB>(l32)) << 4));
-  uint32_t tro[2][DT];
+  uint32_t aoff[KS];  // A rows of S / dP: Q (P wave) or dO (dS wave)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aoff[ks] = opaque((pwave ? Q_OFF : O_OFF) + (rbase ^ (ks << 5)));
+  uint32_t toff[2][DT];  // transpose reads for dV / dK: dO (P wave) or Q (dS wave)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    tro[0][dt] = tr_offset<ROWB>(lane, dt, 0);
-    tro[1][dt] = tr_offset<ROWB>(lane, dt, 1);
+    toff[0][dt] = opaque((pwave ? O_OFF : Q_OFF) + tr_offset<ROWB>(lane, dt, 0));
+    toff[1][dt] = opaque((pwave ? O_OFF : Q_OFF) + tr_offset<ROWB>(lane, dt, 1));
   }
+  const uint32_t soff = opaque(S_OFF + 16 * hf);                      // rows 8 m + 4 hf ..
+  const uint32_t xoff = opaque(X_OFF + pw * 2 * XBYTES + 16 * lane);  // P exchange, C layout
+
   f32x16 acc[DT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) zero_agpr(acc[dt]);
 
   constexpr int PF = 3;
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  auto opaque = [](uint32_t x) {
-    asm volatile("" : "+v"(x));
-    return x;
-  };
-  // P of the pair's current half, C layout: register chunk c of lane l at
-  // 16 bytes x (64 c + l), so that each 16-lane pass of a store or load
-  // covers 256 consecutive bytes
-  float* xb0 = (float*)(smem + NBUF * BUF + pw * 2 * XBYTES);
+  // P of the pair's current half in C layout: register chunk c of lane l at
+  // 16 bytes x (64 c + l), so that each 16-lane pass covers 256 bytes
 
-  auto step = [&](int hh) {
-    const int t = hh >> 1;
-    const char* tile = (const char*)smem + (t % NBUF) * BUF;
-    const char* half = tile + (hh & 1) * 32 * ROWB;
-    const float* sl = (const float*)(tile + 2 * TBYTES) + 32 * (hh & 1);
-    float* xb = xb0 + (hh & 1) * (XBYTES / 4);
+  auto step = [&](int t, auto slot_t, auto half_t) {
+    constexpr int SLOT = decltype(slot_t)::value;
+    constexpr int HALF = decltype(half_t)::value;
+    constexpr int CA = SLOT * TBYTES + HALF * 32 * ROWB;      // half's rows in its ring
+    constexpr int CS = SLOT * SBYTES + HALF * 32 * 4;         // half's lse (Dq: + 256)
+    constexpr int CX = HALF * XBYTES;
     // ---- S = Q K^T (P wave) or dP = dO V^T (dS wave)
-    const char* an = half + (pwave ? 0 : TBYTES);
-    const uint32_t rb = opaque(rbase);
     bf16x8 af[KS];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) af[i] = *reinterpret_cast<const bf16x8*>(an + (rb ^ (i << 5)));
+    for (int i = 0; i < PF; ++i) af[i] = *reinterpret_cast<const bf16x8*>(smem + aoff[i] + CA);
     f32x16 X;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -405,27 +419,27 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
       } else {
         X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], brow[ks], X, 0, 0, 0);
       }
-      if (ks + PF < KS) af[ks + PF] = *reinterpret_cast<const bf16x8*>(an + (rb ^ ((ks + PF) << 5)));
+      if (ks + PF < KS) af[ks + PF] = *reinterpret_cast<const bf16x8*>(smem + aoff[ks + PF] + CA);
     }
     fence();
     if (pwave) {
       // P = exp2(S scale log2e - lse log2e), the masks, then P to the pair
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * m + 4 * hf);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(smem + soff + CS + 32 * m);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           X[4 * m + u] = __builtin_amdgcn_exp2f(fmaf(X[4 * m + u], a.scale2, -l4[u] * kLog2e));
       }
       // rows past the tile's end repeat its last row: P = 0 there
-      const int vrows = rows_of(t) - 32 * (hh & 1);
+      const int vrows = rows_of(t) - 32 * HALF;
       if (vrows < 32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + 4 * hf + (r & 3) >= vrows) X[r] = 0.f;
       }
       const bool own = t >= n_hist;
-      const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile + 32 * (hh & 1);
+      const int qpos0 = own_q0 + (t - n_hist) * kBwdQTile + 32 * HALF;
       if (own && kw + kBwdKeysPerWave - 1 > qpos0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -433,27 +447,26 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<f32x4*>(xb + 4 * (64 * c + lane)) =
+        *reinterpret_cast<f32x4*>(smem + xoff + CX + 1024 * c) =
             f32x4{X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]};
     }
     lds_barrier();  // P of this half is in LDS
     if (!pwave) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(xb + 4 * (64 * c + lane));
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kBwdQTile + 8 * c + 4 * hf);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(smem + xoff + CX + 1024 * c);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(smem + soff + CS + 256 + 32 * c);
 #pragma unroll
         for (int u = 0; u < 4; ++u) X[4 * c + u] = p4[u] * (X[4 * c + u] - d4[u]);
       }
     }
     // ---- dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave)
-    const char* tb = half + (pwave ? TBYTES : 0);
     bf16x8 xb16[2];
     xb16[0] = regs_to_bf16(X, 0);
     xb16[1] = regs_to_bf16(X, 1);
     constexpr int NB = 2 * DT;  // MFMA i: dt = i / 2, s = i % 2
     auto trf = [&](int i) {
-      return tr_frag(tb + (i & 1) * 16 * ROWB, tro[0][i >> 1], tro[1][i >> 1]);
+      return tr_frag(smem + CA + (i & 1) * 16 * ROWB, toff[0][i >> 1], toff[1][i >> 1]);
     };
     bf16x8 tf[NB];
 #pragma unroll
@@ -469,22 +482,36 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
     }
     fence();
   };
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  using c2 = std::integral_constant<int, 2>;
+  // tile t in slot SLOT = t % 3: its two halves, then the barrier
+  auto tile = [&](int t, auto slot_t) {
+    constexpr int SLOT = decltype(slot_t)::value;
+    // every wave is past tile t - 1: its slot takes tile t + 2
+    if (t + 2 < ntiles) issue_tile(t + 2, std::integral_constant<int, (SLOT + 2) % NBUF>());
+    if (w == 1 && t + 4 < n_hist) issue_list(t + 4);
+    step(t, slot_t, c0());
+    step(t, slot_t, c1());
+    // everything issued before this iteration has landed (tile t + 1, the
+    // list slice of tile t + 3); this iteration's loads stay in flight
+    tile_barrier(issued_in(t));
+  };
 
   if (w == 1)
     for (int x = 0; x < 4 && x < n_hist; ++x) issue_list(x);
   __syncthreads();  // list slices of tiles 0 - 3
-  for (int x = 0; x < 2 && x < ntiles; ++x) issue_tile(x, x);
+  if (ntiles > 0) issue_tile(0, c0());
+  if (ntiles > 1) issue_tile(1, c1());
   __syncthreads();  // tiles 0 and 1
-  for (int t = 0; t < ntiles; ++t) {
-    // every wave is past tile t - 1: its slot takes tile t + 2
-    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NBUF);
-    if (w == 1 && t + 4 < n_hist) issue_list(t + 4);
-    step(2 * t);
-    step(2 * t + 1);
-    // everything issued before this iteration has landed (tile t + 1, the
-    // list slice of tile t + 3); this iteration's loads stay in flight
-    tile_barrier(issued_in(t));
+  int t = 0;
+  for (; t + 3 <= ntiles; t += 3) {
+    tile(t, c0());
+    tile(t + 1, c1());
+    tile(t + 2, c2());
   }
+  if (t < ntiles) tile(t, c0());
+  if (t + 1 < ntiles) tile(t + 1, c1());
 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) settle(acc[dt]);
