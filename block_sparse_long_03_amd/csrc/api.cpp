@@ -135,7 +135,7 @@ long long hist_tiles_bound(long long T, long long NB, long long H, long long B, 
 // Backward workspace: the bucket lists and tiles of 128 queries, and
 // Dq = rowsum(dO * O) per (token, head).
 struct BwdWorkspace {
-  size_t counts, offsets, tile_offsets, list, tile_info, dvec, total;
+  size_t counts, offsets, tile_offsets, list, tile_info, dvec, lse2, total;
 };
 
 constexpr int kBwdTileQ = 128;
@@ -160,6 +160,7 @@ BwdWorkspace bwd_workspace_layout(long long T, long long NB, long long H, long l
   w.list = take((size_t)(T * H * (topk > 1 ? topk - 1 : 1)) * 4);
   w.tile_info = take((size_t)bwd_tiles_bound(T, NB, H, topk) * 16);
   w.dvec = take((size_t)(T * H) * 4);
+  w.lse2 = take((size_t)(T * H) * 4);
   w.total = off;
   return w;
 }
@@ -450,12 +451,13 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
   int32_t* list = (int32_t*)(ws + L.list);
   int4* tile_info = (int4*)(ws + L.tile_info);
   float* dvec = (float*)(ws + L.dvec);
+  float* lse2 = (float*)(ws + L.lse2);
   const uint16_t *qb = (const uint16_t*)q, *kb = (const uint16_t*)k, *vb = (const uint16_t*)v,
                  *gb = (const uint16_t*)dout;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = timed("bwd_prep", s, [&] {
-         return moba::launch_bwd_prep(out, out_dtype == MOBA_F32, gb, g, dvec, dq, s);
+         return moba::launch_bwd_prep(out, out_dtype == MOBA_F32, gb, lse, g, dvec, lse2, dq, s);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = timed("bucket", s, [&] {
@@ -465,7 +467,7 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = timed("bwd_kv", s, [&] {
-         return moba::launch_bwd_kv(qb, kb, vb, gb, lse, dvec, g, topk, softmax_scale, list,
+         return moba::launch_bwd_kv(qb, kb, vb, gb, lse2, dvec, g, topk, softmax_scale, list,
                                     offsets, dk, dv, s);
        })) != hipSuccess)
     return hip_fail(e);

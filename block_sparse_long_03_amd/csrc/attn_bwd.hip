@@ -169,12 +169,14 @@ __device__ __forceinline__ bf16x8 regs_to_bf16(const f32x16& x, int s) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: Dq = rowsum(dO * O) (fp32) and dq = 0
+// prep: Dq = rowsum(dO * O) (fp32), lse log2(e) for bwd_kv, and dq = 0
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ out,
                                                        const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
                                                        long long rows, float* __restrict__ dvec,
+                                                       float* __restrict__ lse2,
                                                        float* __restrict__ dq) {
   constexpr int PER = D / 16;  // elements per lane (16 lanes per row)
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -212,7 +214,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && li == 0) dvec[row] = acc;
+  if (row < rows && li == 0) {
+    dvec[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -423,13 +428,14 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
     }
     fence();
     if (pwave) {
-      // P = exp2(S scale log2e - lse log2e), the masks, then P to the pair
+      // P = exp2(S scale log2e - lse log2e) (a.lse holds lse log2e here),
+      // the masks, then P to the pair
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(smem + soff + CS + 32 * m);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          X[4 * m + u] = __builtin_amdgcn_exp2f(fmaf(X[4 * m + u], a.scale2, -l4[u] * kLog2e));
+          X[4 * m + u] = __builtin_amdgcn_exp2f(fmaf(X[4 * m + u], a.scale2, -l4[u]));
       }
       // rows past the tile's end repeat its last row: P = 0 there
       const int vrows = rows_of(t) - 32 * HALF;
@@ -710,13 +716,14 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
-hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const Geo& g,
-                           float* dvec, float* dq, hipStream_t st) {
+hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const float* lse,
+                           const Geo& g, float* dvec, float* lse2, float* dq, hipStream_t st) {
   const long long rows = (long long)g.total_tokens * g.num_heads;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
 #define MOBA_PREP(DD, F)                                                                     \
-  hipLaunchKernelGGL((bwd_prep_kernel<DD, F>), grid, dim3(256), 0, st, out, dout, rows, dvec, dq)
+  hipLaunchKernelGGL((bwd_prep_kernel<DD, F>), grid, dim3(256), 0, st, out, dout, lse, rows, dvec, \
+                     lse2, dq)
   if (g.head_dim == 128) {
     if (out_f32) MOBA_PREP(128, true); else MOBA_PREP(128, false);
   } else {

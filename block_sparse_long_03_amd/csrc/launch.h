@@ -101,10 +101,12 @@ hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const 
 // Backward: Dq = rowsum(dO * O) and dq = 0; dK, dV per (head, block, 128
 // keys) over the block's list and own-block queries; dQ over the forward's
 // historical tiles (tile_info) and own-block tiles, added to dq atomically.
-hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const Geo& g,
-                           float* dvec, float* dq, hipStream_t st);
+// dvec = rowsum(dout * out), lse2 = lse log2(e) (read by bwd_kv), dq = 0
+hipError_t launch_bwd_prep(const void* out, bool out_f32, const uint16_t* dout, const float* lse,
+                           const Geo& g, float* dvec, float* lse2, float* dq, hipStream_t st);
+// lse2: lse log2(e), as bwd_prep writes it
 hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dout, const float* lse, const float* dvec, const Geo& g,
+                         const uint16_t* dout, const float* lse2, const float* dvec, const Geo& g,
                          int topk, float scale, const int32_t* list, const int32_t* offsets,
                          float* dk, float* dv, hipStream_t st);
 hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
