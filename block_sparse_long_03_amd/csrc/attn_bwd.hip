@@ -647,28 +647,36 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQT[dt][r] = 0.f;
 
-  load_chunk(0, 0);
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int b = ch & 1;
-    if (ch + 1 < nchunks) load_chunk(ch + 1, b ^ 1);
-    const char* kt = smem + b * BUF;
-    const char* vt = kt + CBYTES;
+  // per-lane operand offsets held in registers; the chunk loop is unrolled
+  // by buffer, so buffer and sub-chunk offsets ride in the LDS immediate
+  auto opaque = [](uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  uint32_t aoff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aoff[ks] = opaque(rbase ^ (ks << 5));
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    tro[0][dt] = opaque(tro[0][dt]);
+    tro[1][dt] = opaque(tro[1][dt]);
+  }
+  auto chunk = [&](int ch, auto buf_t) {
+    constexpr int BF = decltype(buf_t)::value;
+    if (ch + 1 < nchunks) load_chunk(ch + 1, BF ^ 1);
     const int kp0 = key_lo + ch * kBwdChunk;
 #pragma unroll
     for (int sc = 0; sc < 2; ++sc) {
+      const int ko = BF * BUF + sc * 32 * ROWB;  // compile-time after unrolling
       f32x16 S, dP;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { S[r] = 0.f; dP[r] = 0.f; }
-      const char* kr = kt + sc * 32 * ROWB;
-      const char* vr = vt + sc * 32 * ROWB;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t o = rbase ^ (ks << 5);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + o),
-                                                    qreg[ks], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vr + o),
-                                                     oreg[ks], dP, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(smem + aoff[ks] + ko), qreg[ks], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(smem + aoff[ks] + ko + CBYTES), oreg[ks], dP, 0, 0, 0);
       }
       // S[r], dP[r]: key kp0 + 32 sc + 8 (r / 4) + 4 hf + r % 4, query column l32
       const int kb = kp0 + 32 * sc + 4 * hf;
@@ -682,14 +690,24 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
       const bf16x8 s0 = regs_to_bf16(dP, 0), s1 = regs_to_bf16(dP, 1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dQT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(kr, tro[0][dt], tro[1][dt]),
-                                                          s0, dQT[dt], 0, 0, 0);
         dQT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_frag(kr + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dQT[dt], 0, 0, 0);
+            tr_frag(smem + ko, tro[0][dt], tro[1][dt]), s0, dQT[dt], 0, 0, 0);
+        dQT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag(smem + ko + 16 * ROWB, tro[0][dt], tro[1][dt]), s1, dQT[dt], 0, 0, 0);
       }
     }
-    __syncthreads();  // chunk ch + 1 has landed; buffer b is free again
+    __syncthreads();  // chunk ch + 1 has landed; buffer BF is free again
+  };
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  load_chunk(0, 0);
+  __syncthreads();
+  int ch = 0;
+  for (; ch + 2 <= nchunks; ch += 2) {
+    chunk(ch, c0());
+    chunk(ch + 1, c1());
   }
+  if (ch < nchunks) chunk(ch, c0());
 
   // ---- dq += scale dQ: through LDS, so that each atomic instruction covers
   //      one query row's consecutive dims
