@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,8 +35,31 @@ CFLAGS = [
 
 
 # per-source code generation options: the backward kernels keep MFMA
-# operands and results in VGPRs (their register use fits without spills then)
-SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# operands and results in VGPRs (their register use fits without spills then);
+# its resource report is checked below
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                                 "-Rpass-analysis=kernel-resource-usage"]}
+
+# Kernels that must not use scratch memory: bwd_kv_pair_kernel's tile barrier
+# lets exactly the wave's own LDS DMA of the iteration stay in flight
+# (s_waitcnt vmcnt(n)), which is only right while no other vector-memory
+# instruction, such as a register spill to scratch, sits in its loop.
+NO_SCRATCH = {"attn_bwd.hip": ["bwd_kv_pair_kernel"]}
+
+
+def _check_scratch(src, report):
+    """Raises if a kernel listed in NO_SCRATCH reports scratch use."""
+    current = None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            current = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and current and any(k in current for k in NO_SCRATCH.get(src, [])):
+            if int(m.group(1)) != 0:
+                raise RuntimeError(f"{current} in {src} uses {m.group(1)} bytes of scratch per lane;"
+                                   " its vmcnt accounting assumes none")
 
 
 def _compile(src, build_dir=BUILD, defines=()):
@@ -45,6 +69,8 @@ def _compile(src, build_dir=BUILD, defines=()):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if src in NO_SCRATCH:
+        _check_scratch(src, r.stderr)
     return obj
 
 
