@@ -323,8 +323,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; MoBA shards by head "
-                          "and the multi-GPU path is not built", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the library runs on one GPU; MoBA shards by head, and "
+                          "no multi-GPU path is implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

@@ -68,7 +68,7 @@ typedef enum moba_dtype {
   MOBA_BF16 = 1
 } moba_dtype;
 
-/* Library ABI version (MOBA_API_VERSION of the build). */
+/* ABI version of the loaded library (its MOBA_API_VERSION). */
 int moba_api_version(void);
 
 /* Human-readable name of a moba_status; never NULL. */
