@@ -223,19 +223,23 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
 
 def measured_peaks(torch, moba, dev):
     """The rates this GPU sustains, to set next to the published peaks: the
-    library's bf16 MFMA probe (register operands only, two waves per SIMD)
-    and a plain 4 GiB device copy (read + write), each timed with events on
-    the current stream after a warmup."""
+    library's bf16 MFMA probes (two waves per SIMD; fixed register operands,
+    random register operands, random operands with B read from LDS) and a
+    plain 4 GiB device copy (read + write), each timed with events on the
+    current stream after a warmup."""
     wg = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
-    moba.probe_mfma_rate(wg, 1000, sink)
-    iters = 1000000
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    flops = moba.probe_mfma_rate(wg, iters, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    mfma = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    iters = 1000000
+    rates = {}
+    for operands, key in ((0, "mfma_bf16_tflops"), (1, "mfma_bf16_random_tflops"),
+                          (2, "mfma_bf16_random_lds_tflops")):
+        moba.probe_mfma_rate(wg, 1000, sink, operands)
+        e0.record()
+        flops = moba.probe_mfma_rate(wg, iters, sink, operands)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[key] = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
     n = 1 << 30
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -248,11 +252,13 @@ def measured_peaks(torch, moba, dev):
     copy = 3 * 2 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, sink
     torch.cuda.empty_cache()
-    return {"mfma_bf16_tflops": mfma, "hbm_copy_gbps": copy,
+    return {**rates, "hbm_copy_gbps": copy,
             "spec_mfma_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbps": PEAK_HBM_GBPS,
             "method": f"moba_probe_mfma_rate: {wg} workgroups x 4 waves x 4 independent chains "
-                      f"x {iters} v_mfma_f32_32x32x16_bf16; copy: 3 x torch copy of 4 GiB fp32 "
-                      "(bytes read + written)"}
+                      f"x {iters} v_mfma_f32_32x32x16_bf16, on one fixed low-entropy operand "
+                      "pair, on random bf16 operands cycling through 8 register sets, and on "
+                      "random operands with B read from LDS per product; copy: 3 x torch copy "
+                      "of 4 GiB fp32 (bytes read + written)"}
 
 
 def measure_bwd(torch, inputs, moba, w, dev, steps, warmup):
@@ -473,6 +479,8 @@ def main():
         pk = measured_peaks(torch, moba, dev)
         rec["measured_peaks"] = pk
         rec["roofline"]["frac_of_measured_peak"] = rec["roofline"]["achieved"] / pk["mfma_bf16_tflops"]
+        rec["roofline"]["frac_of_measured_random_lds_peak"] = (
+            rec["roofline"]["achieved"] / pk["mfma_bf16_random_lds_tflops"])
     print(json.dumps(rec), flush=True)
 
 

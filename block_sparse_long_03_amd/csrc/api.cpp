@@ -479,9 +479,13 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
   return MOBA_OK;
 }
 
-moba_status moba_probe_mfma_rate(int workgroups, int iterations, float* sink, void* stream) {
-  if (workgroups < 1 || iterations < 1 || !sink) return MOBA_ERR_INVALID_ARG;
-  hipError_t e = moba::launch_mfma_rate(workgroups, iterations, sink, (hipStream_t)stream);
+moba_status moba_probe_mfma_rate(int workgroups, int iterations, int operands, float* sink,
+                                 void* stream) {
+  if (workgroups < 1 || iterations < 1 || !sink || operands < 0 || operands > 2 ||
+      (operands != 0 && iterations % 8 != 0))
+    return MOBA_ERR_INVALID_ARG;
+  hipError_t e =
+      moba::launch_mfma_rate(workgroups, iterations, operands, sink, (hipStream_t)stream);
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 

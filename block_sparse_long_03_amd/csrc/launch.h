@@ -116,7 +116,10 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 // Measurement support: `workgroups` x 4 waves, each running 4 independent
 // chains of `iterations` 32x32x16 bf16 MFMAs (2 * 32 * 32 * 16 flops each);
-// sink holds workgroups * 256 floats.
-hipError_t launch_mfma_rate(int workgroups, int iterations, float* sink, hipStream_t st);
+// operands 0 = fixed register operands, 1 = random register operands,
+// 2 = random operands with B read from LDS (iterations a multiple of 8 for
+// 1 and 2); sink holds workgroups * 256 floats.
+hipError_t launch_mfma_rate(int workgroups, int iterations, int operands, float* sink,
+                            hipStream_t st);
 
 }  // namespace moba

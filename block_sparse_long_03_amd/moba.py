@@ -26,6 +26,8 @@ MOBA_ERR_WORKSPACE_TOO_SMALL = -3
 MOBA_ERR_HIP = -4
 MOBA_F32 = 0
 MOBA_BF16 = 1
+# the MOBA_API_VERSION of include/moba.h these bindings are written for
+API_VERSION = 2
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
@@ -88,7 +90,7 @@ def lib():
     L.moba_dense_causal_fwd.restype = i32
     L.moba_dense_causal_fwd.argtypes = [vp, vp, vp, i32] + geo + [f32, vp, i32, vp, vp, sz, vp]
     L.moba_probe_mfma_rate.restype = i32
-    L.moba_probe_mfma_rate.argtypes = [i32, i32, vp, vp]
+    L.moba_probe_mfma_rate.argtypes = [i32, i32, i32, vp, vp]
     L.moba_profiler_create.restype = i32
     L.moba_profiler_create.argtypes = [ctypes.POINTER(vp)]
     L.moba_profiler_attach.restype = i32
@@ -102,6 +104,10 @@ def lib():
     L.moba_profiler_names.argtypes = [vp, ctypes.c_char_p, sz]
     L.moba_profiler_destroy.restype = None
     L.moba_profiler_destroy.argtypes = [vp]
+    if L.moba_api_version() != API_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.moba_api_version()}, the bindings "
+                           f"expect {API_VERSION}: rebuild it with "
+                           "`python -m block_sparse_long_03_amd.build`")
     _lib = L
     return L
 
@@ -407,10 +413,11 @@ def layer_forward(mode, q, k, v, geom, topk, scale, out_dtype=None, workspace=No
     raise ValueError(f"unknown attention mode {mode!r}")
 
 
-def probe_mfma_rate(workgroups, iterations, sink, stream=None):
-    """Launches the bf16 MFMA rate probe (measurement support); sink: float32
-    device tensor of at least workgroups * 256 elements.  Returns its flop
-    count."""
+def probe_mfma_rate(workgroups, iterations, sink, operands=0, stream=None):
+    """Launches the bf16 MFMA rate probe (measurement support); operands 0 =
+    fixed register operands, 1 = random register operands, 2 = random
+    operands with B read from LDS; sink: float32 device tensor of at least
+    workgroups * 256 elements.  Returns its flop count."""
     _check("moba_probe_mfma_rate", lib().moba_probe_mfma_rate(
-        int(workgroups), int(iterations), _ptr(sink), _stream(stream)))
+        int(workgroups), int(iterations), int(operands), _ptr(sink), _stream(stream)))
     return workgroups * 4 * 4 * iterations * 2 * 32 * 32 * 16

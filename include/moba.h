@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOBA_API_VERSION 1
+#define MOBA_API_VERSION 2
 
 typedef enum moba_status {
   MOBA_OK = 0,
@@ -290,16 +290,25 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
  *   moba_profiler_destroy  frees p (detach it first)
  */
 /*
- * Measurement support (not part of the computation): a sustained bf16 MFMA
- * rate probe.  Launches `workgroups` workgroups of 4 waves; every wave runs
- * 4 independent chains of `iterations` v_mfma_f32_32x32x16_bf16 on register
- * operands (no memory traffic), i.e. workgroups * 4 * 4 * iterations * 32768
- * flops.  The caller times it (events on `stream`) to obtain the rate the
- * chip sustains at the clock it holds under full matrix load.
+ * Measurement support (not part of the computation): sustained bf16 MFMA
+ * rate probes.  Launches `workgroups` workgroups of 4 waves; every wave runs
+ * 4 independent chains of `iterations` v_mfma_f32_32x32x16_bf16, i.e.
+ * workgroups * 4 * 4 * iterations * 32768 flops.  `operands` selects the
+ * data the products see:
+ *   0  one fixed, low-entropy operand pair in registers (no memory traffic)
+ *   1  random bf16 operands cycling through eight register sets
+ *   2  random register A operands and a random B operand read from LDS for
+ *      every product (1 KiB per wave per MFMA)
+ * The caller times it (events on `stream`) to obtain the rate the chip
+ * sustains at the clock it holds under that load.
  *   sink  device buffer of at least workgroups * 256 floats (written; the
  *         values only keep the products from being optimised away)
+ * Returns MOBA_ERR_INVALID_ARG for workgroups or iterations below 1, a null
+ * sink, operands outside 0..2, or iterations not a multiple of 8 with
+ * operands 1 or 2.
  */
-moba_status moba_probe_mfma_rate(int workgroups, int iterations, float* sink, void* stream);
+moba_status moba_probe_mfma_rate(int workgroups, int iterations, int operands, float* sink,
+                                 void* stream);
 
 typedef struct moba_profiler moba_profiler;
 moba_status moba_profiler_create(moba_profiler** out);

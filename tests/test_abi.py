@@ -39,6 +39,7 @@ def test_exports_every_declared_function(L):
 def test_version_and_status_strings(L):
     text = open(HEADER).read()
     assert L.moba_api_version() == int(re.search(r"MOBA_API_VERSION (\d+)", text).group(1))
+    assert L.moba_api_version() == moba.API_VERSION
     for code, name in [(0, "MOBA_OK"), (-1, "MOBA_ERR_INVALID_ARG"), (-2, "MOBA_ERR_UNSUPPORTED"),
                        (-3, "MOBA_ERR_WORKSPACE_TOO_SMALL"), (-4, "MOBA_ERR_HIP")]:
         assert L.moba_status_str(code).decode() == name
@@ -123,9 +124,13 @@ def test_hybrid_schedule():
 
 def test_probe_arguments(L):
     E = moba.MOBA_ERR_INVALID_ARG
-    assert L.moba_probe_mfma_rate(0, 10, FAKE, None) == E
-    assert L.moba_probe_mfma_rate(4, 0, FAKE, None) == E
-    assert L.moba_probe_mfma_rate(4, 10, None, None) == E
+    assert L.moba_probe_mfma_rate(0, 10, 0, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 0, 0, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 10, 0, None, None) == E
+    assert L.moba_probe_mfma_rate(4, 16, 3, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 16, -1, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 12, 1, FAKE, None) == E
+    assert L.moba_probe_mfma_rate(4, 12, 2, FAKE, None) == E
 
 
 def test_unsupported(L):
