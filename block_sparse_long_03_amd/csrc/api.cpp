@@ -118,17 +118,19 @@ long long hist_entries_bound(const moba::Geo& g, int topk) {
 }
 
 long long hist_tiles_bound(const moba::Geo& g, int topk) {
-  return moba::hist_tiles_bound(g.total_tokens, g.total_blocks, g.num_heads, g.block_size, topk);
+  return moba::hist_tiles_bound(g.total_tokens, g.total_blocks, g.num_heads, g.head_dim,
+                                g.block_size, topk);
 }
 
 }  // namespace
 
 namespace moba {
 
-long long hist_tiles_bound(long long T, long long NB, long long H, long long B, long long topk) {
+long long hist_tiles_bound(long long T, long long NB, long long H, long long D, long long B,
+                           long long topk) {
   if (topk < 2) return 0;
   const long long e = T * H * (topk - 1);
-  const long long tq = mfma_tile_q((int)B);
+  const long long tq = hist_tile_q((int)B, (int)D);
   return (e + tq - 1) / tq + H * NB;
 }
 
@@ -182,7 +184,7 @@ AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long l
   w.lse_part = take((size_t)(T * H * topk) * 4);
   w.o_part = take((size_t)(T * H * topk * D) * (bf16 ? 2 : 4));
   w.vt = take(bf16 ? (size_t)(NB * B * H * D) * 2 : 0);
-  w.tile_info = take(bf16 ? (size_t)hist_tiles_bound(T, NB, H, B, topk) * 16 : 0);
+  w.tile_info = take(bf16 ? (size_t)hist_tiles_bound(T, NB, H, D, B, topk) * 16 : 0);
   w.vmax = take((size_t)H * 4);
   w.total = off;
   return w;
@@ -367,8 +369,9 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
         hipSuccess)
       return hip_fail(e);
     if ((e = timed("bucket", s, [&] {
-           return moba::launch_bucket(block_idx, g, topk, moba::mfma_tile_q(g.block_size), counts, offsets,
-                                      tile_offsets, list, tile_info, tiles, s);
+           return moba::launch_bucket(block_idx, g, topk,
+                                      moba::hist_tile_q(g.block_size, g.head_dim), counts,
+                                      offsets, tile_offsets, list, tile_info, tiles, s);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_hist", s, [&] {

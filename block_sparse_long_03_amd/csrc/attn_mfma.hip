@@ -35,7 +35,8 @@
 
 namespace moba {
 
-enum { kModeHist = 0, kModeOwn = 1, kModeDense = 2 };
+// kModeHistRes: historical tiles with the whole KV block resident in LDS
+enum { kModeHist = 0, kModeOwn = 1, kModeDense = 2, kModeHistRes = 3 };
 
 // max / sum of a value and the same register of lane (lane ^ 32): one
 // v_permlane32_swap, which hands each half the other half's value
@@ -95,7 +96,10 @@ void attn_mfma_kernel(MfmaArgs a) {
   constexpr int NVI = VBYTES / 1024;
   constexpr int KIW = (NKI + kWaves - 1) / kWaves;  // per wave
   constexpr int VIW = (NVI + kWaves - 1) / kWaves;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  constexpr bool RES = MODE == kModeHistRes;
+  constexpr bool HIST = MODE == kModeHist || RES;
+  static_assert(!RES || kWaves == 8, "resident tiles run 8 waves");
+  __shared__ __attribute__((aligned(1024))) char smem[RES ? kResidentLdsBytes : 2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,8 +111,9 @@ void attn_mfma_kernel(MfmaArgs a) {
   int h, seq_start, seq_len, key_lo, key_hi, gb_base;
   int qtok = -1, qpos = 0x7fffffff;
   long long oidx = 0;
-  if (MODE == kModeHist) {
-    const int4 ti = a.tile_info[blockIdx.x];
+  int4 ti = {0, 0, 0, 0};
+  if (HIST) {
+    ti = a.tile_info[blockIdx.x];
     const int key = ti.x;
     if (key < 0) return;
     h = key / a.NB;
@@ -118,11 +123,13 @@ void attn_mfma_kernel(MfmaArgs a) {
     gb_base = a.cu_blocks[s];
     key_lo = (gb - gb_base) * a.block_size;
     key_hi = min(key_lo + a.block_size, seq_len);
-    const int j = ti.y + w * 32 + l32;
-    if (j < ti.z) {
-      const int ent = a.list[j];
-      qtok = ent / a.topk;
-      oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
+    if (!RES) {
+      const int j = ti.y + w * 32 + l32;
+      if (j < ti.z) {
+        const int ent = a.list[j];
+        qtok = ent / a.topk;
+        oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
+      }
     }
   } else {
     // XCD-contiguous order: the tiles of one block (own) or sequence (dense)
@@ -164,7 +171,7 @@ void attn_mfma_kernel(MfmaArgs a) {
 
   // ---------------- Q fragments (B operand) ----------------
   bf16x8 qreg[KS];
-  {
+  if (!RES) {
     const bool qv = qtok >= 0;
     const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.H + h) * D + 8 * hf;
 #pragma unroll
@@ -261,7 +268,7 @@ void attn_mfma_kernel(MfmaArgs a) {
 
   // S[r] is the score of query column (lane & 31) with key kp + 8 (r / 4) + 4 hf + (r % 4)
   auto mask = [&](f32x16& S, int kp) {
-    if (MODE != kModeHist && kp + 31 > wq_min) {
+    if (!HIST && kp + 31 > wq_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kp + 8 * (r >> 2) + 4 * hf + (r & 3) > qpos) S[r] = -INFINITY;
@@ -317,16 +324,22 @@ void attn_mfma_kernel(MfmaArgs a) {
   };
   auto iteration = [&](int c, f32x16& S0, f32x16& S1, f32x16& N0, f32x16& N1, auto odd_t,
                        auto more_t) {
-    constexpr int CS = decltype(odd_t)::value ? 1 : 0;  // slot of chunk c
-    constexpr int NS = CS ^ 1;                           // slot of chunk c + 1
+    // slots of chunks c and c + 1: their parity in the double buffers; in
+    // resident tiles chunk c sits at c * BUF, added to the operand bases
+    constexpr int CS = RES ? 0 : (decltype(odd_t)::value ? 1 : 0);
+    constexpr int NS = RES ? 0 : CS ^ 1;
     constexpr bool MORE = decltype(more_t)::value;
+    const uint32_t kshift = RES ? (uint32_t)((c + 1) * BUF) : 0u;
+    const uint32_t vshift = RES ? (uint32_t)(c * BUF) : 0u;
     const int kp0 = key_lo + c * kTK;
     mask(S0, kp0);
     mask(S1, kp0 + 32);
-    if (c + 2 < nchunks) load_k(c + 2, CS);
-    if (MORE) load_v(NS);
-    const uint32_t kb = opaque(kbase0);
-    const uint32_t vb = opaque(vbase0);
+    if (!RES) {
+      if (c + 2 < nchunks) load_k(c + 2, CS);
+      if (MORE) load_v(NS);
+    }
+    const uint32_t kb = opaque(kbase0 + kshift);
+    const uint32_t vb = opaque(vbase0 + vshift);
     const float base_old = m_use == -INFINITY ? 0.f : m_use;
     bf16x8 kf[KS], kg[KS];
     f16x8 vf[NPV], vg[NPV];
@@ -377,7 +390,7 @@ void attn_mfma_kernel(MfmaArgs a) {
       }
     }
     // ---- B
-    const uint32_t kb2 = opaque(kbase0);
+    const uint32_t kb2 = opaque(kbase0 + kshift);
     f16x8 P0[2], P1[2];
     if (MORE) {
 #pragma unroll
@@ -413,62 +426,128 @@ void attn_mfma_kernel(MfmaArgs a) {
   };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
-  load_k(0, 0);
-  load_v(0);
-  if (nchunks > 1) load_k(1, 1);
-  __syncthreads();
-  f32x16 S0 = qk(kbase0, 0, 0);
-  f32x16 S1 = qk(kbase0, 0, 1);
-  f32x16 N0, N1;
-  __syncthreads();  // K(0) is read: its slot takes K(2)
-  int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    iteration(c, S0, S1, N0, N1, no(), yes());
-    __syncthreads();  // K(c + 2) and V(c + 1) have landed; K(c + 1) and V(c) are read
-    iteration(c + 1, N0, N1, S0, S1, yes(), yes());
+  if constexpr (!RES) {
+    load_k(0, 0);
+    load_v(0);
+    if (nchunks > 1) load_k(1, 1);
     __syncthreads();
-  }
-  if (c + 1 < nchunks) {
-    iteration(c, S0, S1, N0, N1, no(), yes());
-    __syncthreads();
-    iteration(c + 1, N0, N1, S0, S1, yes(), no());
-  } else {
-    iteration(c, S0, S1, N0, N1, no(), no());
-  }
+    f32x16 S0 = qk(kbase0, 0, 0);
+    f32x16 S1 = qk(kbase0, 0, 1);
+    f32x16 N0, N1;
+    __syncthreads();  // K(0) is read: its slot takes K(2)
+    int c = 0;
+    for (; c + 2 < nchunks; c += 2) {
+      iteration(c, S0, S1, N0, N1, no(), yes());
+      __syncthreads();  // K(c + 2) and V(c + 1) have landed; K(c + 1) and V(c) are read
+      iteration(c + 1, N0, N1, S0, S1, yes(), yes());
+      __syncthreads();
+    }
+    if (c + 1 < nchunks) {
+      iteration(c, S0, S1, N0, N1, no(), yes());
+      __syncthreads();
+      iteration(c + 1, N0, N1, S0, S1, yes(), no());
+    } else {
+      iteration(c, S0, S1, N0, N1, no(), no());
+    }
 
-  // ---------------- epilogue ----------------
-  if (qtok < 0) return;  // both lanes of a query column take the same branch
-  float out_scale = 1.f;
-  if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
-  const float l_tot = sum_with_partner(l_run);
-  const float inv = out_scale / l_tot;
-  const float lse_val = (m_use + log2f(l_tot)) * kLn2;
-  // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
-  if (MODE == kModeDense && !OUT_BF16) {
-    float* op = (float*)a.o_out + (size_t)oidx * D;
+    // ---------------- epilogue ----------------
+    if (qtok < 0) return;  // both lanes of a query column take the same branch
+    float out_scale = 1.f;
+    if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
+    const float l_tot = sum_with_partner(l_run);
+    const float inv = out_scale / l_tot;
+    const float lse_val = (m_use + log2f(l_tot)) * kLn2;
+    // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
+    if (MODE == kModeDense && !OUT_BF16) {
+      float* op = (float*)a.o_out + (size_t)oidx * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv, O[dt][4 * g + 2] * inv,
-                    O[dt][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
-      }
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4 = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv, O[dt][4 * g + 2] * inv,
+                      O[dt][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
+        }
+    } else {
+      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
+          const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
+          u32x2 v2;
+          if (MODE == kModeDense) v2 = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          else v2 = u32x2{pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
+          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+        }
+    }
+    if (hf == 0) a.lse_out[oidx] = lse_val;
   } else {
-    uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
-        const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
-        u32x2 v2;
-        if (MODE == kModeDense) v2 = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-        else v2 = u32x2{pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+    // ---------------- resident passes ----------------
+    // the whole block once, chunk ch in slot ch; LDS is read-only afterwards,
+    // so each wave runs its passes of 32 gathered queries without barriers
+    for (int ch = 0; ch < nchunks; ++ch) {
+      load_k(ch, ch);
+      load_v(ch);
+    }
+    __syncthreads();
+    f32x16 S0, S1, N0, N1;
+    for (int r0 = ti.y + w * 32; r0 < ti.z; r0 += kWaves * 32) {
+      const int j = r0 + l32;
+      qtok = -1;
+      if (j < ti.z) {
+        const int ent = a.list[j];
+        qtok = ent / a.topk;
+        oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
       }
+      {
+        const bool qv = qtok >= 0;
+        const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.H + h) * D + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 wv = {0u, 0u, 0u, 0u};
+          if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+          qreg[ks] = __builtin_bit_cast(bf16x8, wv);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+      m_use = -INFINITY;
+      l_run = 0.f;
+      S0 = qk(kbase0, 0, 0);
+      S1 = qk(kbase0, 0, 1);
+      int c = 0;
+      for (; c + 2 < nchunks; c += 2) {
+        iteration(c, S0, S1, N0, N1, no(), yes());
+        iteration(c + 1, N0, N1, S0, S1, yes(), yes());
+      }
+      if (c + 1 < nchunks) {
+        iteration(c, S0, S1, N0, N1, no(), yes());
+        iteration(c + 1, N0, N1, S0, S1, yes(), no());
+      } else {
+        iteration(c, S0, S1, N0, N1, no(), no());
+      }
+      // fp16 partial (V units) and lse of the pass's rows
+      if (qtok >= 0) {
+        const float l_tot = sum_with_partner(l_run);
+        const float inv = 1.f / l_tot;
+        uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
+            const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
+            const u32x2 v2 = {pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
+            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
+          }
+        if (hf == 0) a.lse_out[oidx] = (m_use + log2f(l_tot)) * kLn2;
+      }
+    }
   }
-  if (hf == 0) a.lse_out[oidx] = lse_val;
 }
 
 static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, const Geo& g,
@@ -507,9 +586,18 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
   a.tile_info = tile_info;
   a.o_out = o_part;
   a.lse_out = lse_part;
-  // tile_info was cut into tiles of mfma_tile_q(block_size) queries
-  const int waves = mfma_waves(g.block_size);
+  // tile_info was cut into tiles of hist_tile_q(block_size, head_dim) queries
   dim3 grid((unsigned)max_tiles);
+  if (hist_resident(g.block_size, g.head_dim)) {
+    if (g.head_dim == 128)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, kModeHistRes, true, 8>), grid, dim3(64 * 8), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<64, kModeHistRes, true, 8>), grid, dim3(64 * 8), 0,
+                         st, a);
+    return hipGetLastError();
+  }
+  const int waves = mfma_waves(g.block_size);
   if (g.head_dim == 128) launch_mfma<128, kModeHist, true>(waves, grid, st, a);
   else launch_mfma<64, kModeHist, true>(waves, grid, st, a);
   return hipGetLastError();

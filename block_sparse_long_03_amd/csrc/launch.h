@@ -30,6 +30,21 @@ inline int mfma_waves(int key_range) { return key_range >= 1024 ? 8 : 4; }
 inline int mfma_tile_q(int key_range) { return 32 * mfma_waves(key_range); }
 constexpr int kF32TileQ = 1;
 
+// Resident historical tiles: when a whole KV block fits in LDS (K and V^T of
+// B keys: B * d * 4 bytes <= 128 KiB, e.g. B <= 256 at d = 128), an 8-wave
+// workgroup loads it once and runs kResidentPasses passes of 256 gathered
+// queries against it, so the block is fetched once per 1024 queries.
+constexpr int kResidentLdsBytes = 128 * 1024;
+constexpr int kResidentPasses = 4;
+inline bool hist_resident(int block_size, int head_dim) {
+  return (long long)block_size * head_dim * 4 <= kResidentLdsBytes;
+}
+// rows of one historical tile (one workgroup of the historical grid)
+inline int hist_tile_q(int block_size, int head_dim) {
+  return hist_resident(block_size, head_dim) ? 32 * 8 * kResidentPasses
+                                             : mfma_tile_q(block_size);
+}
+
 // Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
 struct AttnWorkspace {
   size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, tile_info, vmax, total;
@@ -37,9 +52,10 @@ struct AttnWorkspace {
 AttnWorkspace attn_workspace_layout(bool bf16, long long total_tokens, long long total_blocks,
                                     long long num_heads, long long head_dim,
                                     long long block_size, long long topk);
-// Upper bound on the number of historical tiles of mfma_tile_q(block_size) rows.
+// Upper bound on the number of historical tiles of hist_tile_q(block_size,
+// head_dim) rows.
 long long hist_tiles_bound(long long total_tokens, long long total_blocks, long long num_heads,
-                           long long block_size, long long topk);
+                           long long head_dim, long long block_size, long long topk);
 size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_heads,
                              long long head_dim, long long block_size);
 

@@ -204,6 +204,10 @@ EDGE = [
     # block size >= 1024: 256-query historical tiles (8 waves), ragged tails
     inputs.custom([3000, 2100, 700], 2, 128, 1024, 3, "bf16", name="B1024-ragged"),
     inputs.custom([4100], 2, 64, 1024, 3, "bf16", name="d64-B1024"),
+    # whole KV block resident in LDS: lists of several 1024-query tiles, each
+    # run as up to 4 passes per wave; d = 64 at the largest resident B
+    inputs.custom([6000, 2500], 2, 128, 256, 6, "bf16", name="B256-resident-multitile"),
+    inputs.custom([5000, 1500], 2, 64, 512, 4, "bf16", name="d64-B512-resident"),
 ]
 
 
