@@ -35,7 +35,7 @@ constexpr int kF32TileQ = 1;
 // workgroup loads it once and runs kResidentPasses passes of 256 gathered
 // queries against it, so the block is fetched once per 1024 queries.
 constexpr int kResidentLdsBytes = 128 * 1024;
-constexpr int kResidentPasses = 4;
+constexpr int kResidentPasses = 8;
 inline bool hist_resident(int block_size, int head_dim) {
   return (long long)block_size * head_dim * 4 <= kResidentLdsBytes;
 }
