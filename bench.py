@@ -48,6 +48,61 @@ def dense_pairs(seqlens, H):
     return H * sum(L * (L + 1) // 2 for L in seqlens)
 
 
+# tile policy of the library's attention grids (launch.h): resident
+# historical tiles when K and V^T of a block fit in 128 KiB of LDS, else
+# 32-query columns on 8 waves (B >= 1024) or 4; own-block tiles of 4 waves
+RESIDENT_LDS_BYTES = 128 * 1024
+
+
+def issued_pairs(list_lengths, seqlens, B, d):
+    """(query, key) pairs the attention kernels put through the MFMA units,
+    padding included: historical rows rounded up to the rows a tile computes
+    (32 per wave pass in resident tiles, whole tiles otherwise) against all B
+    keys of the block, and own-block tiles of 128 query columns against
+    64-key chunks up to their last query.  list_lengths holds the number of
+    historical selections of each (head, KV block)."""
+    import numpy as np
+    n = np.asarray(list_lengths, dtype=np.int64)
+    if B * d * 4 <= RESIDENT_LDS_BYTES:
+        rows = (n + 31) // 32 * 32
+    else:
+        tq = 32 * (8 if B >= 1024 else 4)
+        rows = (n + tq - 1) // tq * tq
+    hist = int(rows.sum()) * B
+    own = 0
+    for L in seqlens:
+        for blo in range(0, L, B):
+            blen = min(B, L - blo)
+            for q_lo in range(0, blen, 128):
+                q_hi = min(q_lo + 128, blen)
+                own += 128 * 64 * ((q_hi + 63) // 64)
+    return hist, own
+
+
+def list_lengths(torch, idx, seqlens, B):
+    """Historical selections per (head, global KV block) of block_idx
+    [T, H, k] (entries below the query's own block)."""
+    T, H, _ = idx.shape
+    dev = idx.device
+    starts, blocks = [0], [0]
+    for L in seqlens:
+        starts.append(starts[-1] + L)
+        blocks.append(blocks[-1] + (L + B - 1) // B)
+    nb = blocks[-1]
+    cu = torch.tensor(starts, dtype=torch.int64, device=dev)
+    cb = torch.tensor(blocks, dtype=torch.int64, device=dev)
+    tok = torch.arange(T, dtype=torch.int64, device=dev)
+    seq = torch.searchsorted(cu[1:], tok, right=True)
+    c = (tok - cu[seq]) // B
+    counts = torch.zeros(H * nb, dtype=torch.int64, device=dev)
+    for h in range(H):  # one head at a time bounds the temporaries
+        row = idx[:, h, :].to(torch.int64)
+        valid = (row >= 0) & (row < c[:, None])
+        key = h * nb + cb[seq][:, None] + row
+        counts += torch.bincount(key[valid], minlength=H * nb)
+    return counts.cpu().numpy()
+
+
 # sources the historical-attention kernel is built from
 HIST_SOURCES = ("attn_mfma.hip", "common.h", "launch.h")
 
@@ -213,12 +268,13 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
         print(f"[bench] {w.name}: dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
     prof.detach()
     prof.close()
+    lengths = list_lengths(torch, idx, w.seqlens, w.block_size) if w.dtype == "bf16" else None
     del kbar, idx, out, lse
     if not keep:
         del x, q, k, v
         x = None
         torch.cuda.empty_cache()
-    return x, geom, ms_step, kern, dense_ms, rec_dense_stages
+    return x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths
 
 
 def measured_peaks(torch, moba, dev):
@@ -350,7 +406,7 @@ def main():
 
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
-    x, geom, ms_step, kern, dense_ms, rec_dense_stages = measure(
+    x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths = measure(
         torch, inputs, moba, w, dev, args.steps, args.warmup, args.dense_reps, keep=True)
     H, d = w.heads, w.head_dim
     q = x["q"]
@@ -374,6 +430,19 @@ def main():
     # both attention kernels together: 4d flops per attended pair over their summed time
     t_attn = avg_h + (ms_o / max(n_o, 1) if ms_o > 0 else 0.0)
     attn_frac = (flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if t_attn > 0 else None
+    mfma_issued = None
+    if lengths is not None and t_attn > 0:
+        ih, io = issued_pairs(lengths, w.seqlens, w.block_size, d)
+        io *= H
+        mfma_issued = {
+            "historical_pairs": ih, "own_pairs": io, "flops": 4.0 * d * (ih + io),
+            "tflops_over_attention_time": 4.0 * d * (ih + io) / (t_attn * 1e-3) / 1e12,
+            "algorithmic_share": (hist_p + own_p) / (ih + io),
+        }
+    n_g, ms_g = kern.get("gate_topk", (0, 0.0))
+    gate_bytes = (geom.total_tokens * H * d * q.element_size() + geom.total_tokens * H * w.topk * 4
+                  + geom.total_blocks * H * d * 4)
+    gate_gbps = gate_bytes / (ms_g / max(n_g, 1) * 1e-3) / 1e9 if ms_g > 0 else None
     n_p, ms_p = kern.get("pool_keys", (0, 0.0))
     pool_bytes = geom.total_tokens * H * d * q.element_size() + geom.total_blocks * H * d * 4
     pool_gbps = pool_bytes / (ms_p / max(n_p, 1) * 1e-3) / 1e9 if ms_p > 0 else None
@@ -406,6 +475,11 @@ def main():
         "attention_mfma_frac": attn_frac,
         "pool_gbps": pool_gbps,
         "pool_hbm_frac": pool_gbps / PEAK_HBM_GBPS if pool_gbps else None,
+        # gate + top-k: algorithmic bytes (Q read, block_idx written, kbar read once)
+        "gate_gbps": gate_gbps,
+        "gate_hbm_frac": gate_gbps / PEAK_HBM_GBPS if gate_gbps else None,
+        # what the attention kernels put through the MFMA units, tile padding included
+        "mfma_issued": mfma_issued,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -448,8 +522,9 @@ def main():
         # extrapolated from the headline's measured dense rate per causal pair
         big = wo.total_tokens > (1 << 22)
         dense_reps_o = 2 if (args.dense_reps and wname != w.name and not big) else 0
-        _, _, ms_o2, kern_o, dense_o, _ = measure(torch, inputs, moba, wo, dev, steps_o,
-                                                  max(1, args.warmup), dense_reps_o, gate=gate)
+        _, _, ms_o2, kern_o, dense_o, _, _ = measure(torch, inputs, moba, wo, dev, steps_o,
+                                                     max(1, args.warmup), dense_reps_o,
+                                                     gate=gate)
         if dense_o is None and wname == w.name:
             dense_o = dense_ms
         pairs_o, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)

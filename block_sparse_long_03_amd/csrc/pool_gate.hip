@@ -349,6 +349,15 @@ __global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int c = p0 / block_size;
   const int k1 = topk - 1;
   const int gb0 = cu_blocks[sid];
+  if (c <= k1) {
+    // at most k - 1 past blocks: all of them are selected, so the rows need
+    // no scores (blocks 0 .. c ascending, the own block last, then -1)
+    for (int i = tid; i < nq * topk; i += kGateWaves * 64) {
+      const int r = i / topk, j = i - r * topk;
+      block_idx[((size_t)(start + p0 + r) * H + h) * topk + j] = j <= c ? j : -1;
+    }
+    return;
+  }
 
   uint32_t tkey[kGateRowsPerWave];
   int32_t tidx[kGateRowsPerWave];

@@ -45,3 +45,52 @@ def test_dense_pairs_is_the_causal_count():
     assert bench.dense_pairs(seqlens, 3) == 3 * sum(L * (L + 1) // 2 for L in seqlens)
     # k >= n: MoBA attends exactly the causal pairs
     assert bench.attended_pairs(seqlens, 64, 64, 3)[0] == bench.dense_pairs(seqlens, 3)
+
+
+def test_issued_pairs_hand_cases():
+    # resident tiles (B 64, d 128): rows round up to 32 per wave pass
+    hist, own = bench.issued_pairs([33, 0, 64], [100], 64, 128)
+    assert hist == (64 + 0 + 64) * 64
+    # own block: blocks of 64 and 36 queries, one 128-column tile of one
+    # 64-key chunk each
+    assert own == 2 * 128 * 64
+    # B 1024: 8-wave tiles of 256 rows; the own block of a 1500-token
+    # sequence: block 0 has 8 tiles (chunks up to 2, 4, .., 16), block 1
+    # (476 queries) 4 tiles (chunks 2, 4, 6, 8)
+    hist, own = bench.issued_pairs([300, 256, 1], [1500], 1024, 128)
+    assert hist == (512 + 256 + 256) * 1024
+    assert own == 128 * 64 * (sum(range(2, 17, 2)) + (2 + 4 + 6 + 8))
+    # B 512 at d 128 is not resident: 4-wave tiles of 128 rows
+    hist, _ = bench.issued_pairs([129], [512], 512, 128)
+    assert hist == 256 * 512
+    # d 64 keeps B 512 resident
+    hist, _ = bench.issued_pairs([129], [512], 512, 64)
+    assert hist == 160 * 512
+
+
+def test_list_lengths_counts_historical_selections():
+    import torch
+    rng = np.random.default_rng(3)
+    seqlens, B, k, H = [700, 0, 129, 300], 64, 4, 3
+    rows = []
+    for L in seqlens:
+        for t in range(L):
+            c = t // B
+            rows.append([mo.select_row(rng.standard_normal(c), c, k)[0] for _ in range(H)])
+    idx = torch.tensor(np.array(rows), dtype=torch.int32)
+    got = bench.list_lengths(torch, idx, seqlens, B)
+    cb = np.concatenate([[0], np.cumsum([(L + B - 1) // B for L in seqlens])])
+    nb = int(cb[-1])
+    want = np.zeros(H * nb, dtype=np.int64)
+    t0 = 0
+    for s, L in enumerate(seqlens):
+        for t in range(L):
+            c = t // B
+            for h in range(H):
+                for b in rows[t0 + t][h]:
+                    if 0 <= b < c:
+                        want[h * nb + cb[s] + b] += 1
+        t0 += L
+    assert np.array_equal(got, want)
+    # every historical selection of a row lands in exactly one list
+    assert got.sum() == sum(H * min(k - 1, t // B) for L in seqlens for t in range(L))
