@@ -1,6 +1,6 @@
 // bf16 MFMA block attention for gfx950 (CDNA4), fp32 accumulation.
 //
-// One tile = up to 128 or 256 query rows (4 waves x 32 or 64) against a contiguous key
+// One tile = up to 128 or 256 query rows (4 or 8 waves x 32) against a contiguous key
 // range of one sequence and head:
 //   historical: the gathered queries that selected KV block j, all B keys of
 //               block j, no mask ("MoBA: Learned Block Sparsity for
@@ -24,7 +24,10 @@
 // K and V^T chunks of 64 keys are double-buffered in LDS and filled by direct
 // global-to-LDS loads (buffer_load_dwordx4 ... lds: each wave instruction
 // writes 1 KiB of consecutive LDS, no registers involved) while the previous chunk
-// is computed; one barrier per chunk.  The LDS tiles are unpadded and
+// is computed; one barrier per chunk.  When a whole block fits in LDS
+// (B * d * 4 bytes <= 128 KiB), historical tiles keep it resident instead:
+// every chunk is loaded once, and each wave then runs several passes of 32
+// gathered queries over the resident chunks with no further barrier.  The LDS tiles are unpadded and
 // XOR-swizzled in 16-byte segments so that the MFMA operand reads are free of
 // bank conflicts: rows of 256 B use segment ^ (row & 15), rows of 128 B use
 // segment ^ ((row >> 1) & 7).
