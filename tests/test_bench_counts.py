@@ -94,3 +94,15 @@ def test_list_lengths_counts_historical_selections():
     assert np.array_equal(got, want)
     # every historical selection of a row lands in exactly one list
     assert got.sum() == sum(H * min(k - 1, t // B) for L in seqlens for t in range(L))
+
+
+def test_issued_pairs_follows_the_launch_policy():
+    """bench.issued_pairs mirrors the tile policy of launch.h: keep the two
+    in step (resident LDS budget, the 8-wave threshold)."""
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "block_sparse_long_03_amd", "csrc", "launch.h")).read()
+    m = re.search(r"constexpr int kResidentLdsBytes = (\d+) \* (\d+);", src)
+    assert m and int(m.group(1)) * int(m.group(2)) == bench.RESIDENT_LDS_BYTES
+    assert re.search(r"return key_range >= 1024 \? 8 : 4;", src)
+    assert re.search(r"return \(long long\)block_size \* head_dim \* 4 <= kResidentLdsBytes;", src)
