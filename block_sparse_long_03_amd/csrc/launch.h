@@ -33,9 +33,9 @@ constexpr int kF32TileQ = 1;
 // Resident historical tiles: when a whole KV block fits in LDS (K and V^T of
 // B keys: B * d * 4 bytes <= 128 KiB, e.g. B <= 256 at d = 128), an 8-wave
 // workgroup loads it once and runs kResidentPasses passes of 256 gathered
-// queries against it, so the block is fetched once per 1024 queries.
+// queries against it, so the block is fetched once per 4096 queries.
 constexpr int kResidentLdsBytes = 128 * 1024;
-constexpr int kResidentPasses = 8;
+constexpr int kResidentPasses = 16;
 inline bool hist_resident(int block_size, int head_dim) {
   return (long long)block_size * head_dim * 4 <= kResidentLdsBytes;
 }

@@ -13,6 +13,8 @@ from block_sparse_long_03_amd import inputs, moba
 from oracle import moba_oracle as mo
 from tests import parity
 
+import bench  # list lengths of a selection (measurement helper)
+
 pytestmark = pytest.mark.gpu
 
 
@@ -204,9 +206,10 @@ EDGE = [
     # block size >= 1024: 256-query historical tiles (8 waves), ragged tails
     inputs.custom([3000, 2100, 700], 2, 128, 1024, 3, "bf16", name="B1024-ragged"),
     inputs.custom([4100], 2, 64, 1024, 3, "bf16", name="d64-B1024"),
-    # whole KV block resident in LDS: lists of several 1024-query tiles, each
-    # run as up to 4 passes per wave; d = 64 at the largest resident B
-    inputs.custom([6000, 2500], 2, 128, 256, 6, "bf16", name="B256-resident-multitile"),
+    # whole KV block resident in LDS: lists longer than one 4096-query tile,
+    # each tile run as up to 16 passes per wave; d = 64 at the largest
+    # resident B
+    inputs.custom([12000, 2500], 2, 128, 256, 12, "bf16", name="B256-resident-multitile"),
     inputs.custom([5000, 1500], 2, 64, 512, 4, "bf16", name="d64-B512-resident"),
 ]
 
@@ -214,6 +217,10 @@ EDGE = [
 @pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
 def test_moba_edge_cases(dev, w):
     x, geom, out, lse, idx = _run(w, dev, seed=77, out_dtype=torch.float32)
+    if w.name == "B256-resident-multitile":
+        # the case must reach a list longer than one resident tile
+        lengths = bench.list_lengths(torch, idx, w.seqlens, w.block_size)
+        assert lengths.max() > 4096, lengths.max()
     T = w.total_tokens
     rows = np.stack(np.meshgrid(np.arange(T), np.arange(w.heads), indexing="ij"), -1).reshape(-1, 2)
     if len(rows) > 3000:
