@@ -129,65 +129,103 @@ def traffic_from_profiles(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, rows_target, seconds):
-    """The fp64 oracle on a bounded sample of query rows of head 0."""
+# per-worker state of the CPU baseline (set in the parent before forking)
+_CPU_JOB = {}
+
+
+def _cpu_worker(h):
+    """The oracle on seeded rows of head h of the bench workload: the head's
+    block pooling once (the oracle's pool_keys_head), then row after row the
+    oracle's own steps 2-5 (gate scores, causal top-k, attended tokens, exact
+    softmax), exactly as moba_reference runs them, until the time budget is
+    spent.  BLAS runs one thread.  Returns (rows done, attended pairs,
+    pooling seconds, row seconds)."""
     import numpy as np
     from oracle import moba_oracle as mo
     try:
         from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    h = 0
-    q = x["q"][:, h:h + 1, :].float().cpu().numpy()
-    k = x["k"][:, h:h + 1, :].float().cpu().numpy()
-    v = x["v"][:, h:h + 1, :].float().cpu().numpy()
-    rng = np.random.default_rng(2000 + w.index)
-    T = w.total_tokens
-    ts = np.sort(rng.choice(T, size=min(rows_target, T), replace=False))
-    rows = np.stack([ts, np.zeros_like(ts)], axis=1)
-    cu = x["cu_seqlens"]
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
+        ctx = None
+    j = _CPU_JOB
+    q, k, v = (j[n][h] for n in ("q", "k", "v"))  # [T, d] fp32 (exact bf16 values)
+    cu = j["cu"]
+    B, topk, scale = j["B"], j["topk"], j["scale"]
+    rng = np.random.default_rng(2000 + j["index"] * 100 + h)
+    ts = np.sort(rng.choice(len(q), size=min(j["rows"], len(q)), replace=False))
     try:
-        # pooled keys of the sampled head first (once per head in a full run)
         t0 = time.perf_counter()
-        mo.moba_reference(q, k, v, cu, w.block_size, w.topk, w.scale, rows=rows[:1])
-        t_first = time.perf_counter() - t0
-        done = 0
+        kbar = {}
+        for s in range(len(cu) - 1):
+            a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+            kbar[s] = mo.pool_keys_head(k[a:a + L], L, B)
+        t_pool = time.perf_counter() - t0
+        done = pairs = 0
         t0 = time.perf_counter()
-        res = None
-        for i in range(1, len(rows), 8):
-            res = mo.moba_reference(q, k, v, cu, w.block_size, w.topk, w.scale,
-                                    rows=rows[i:i + 8])
-            done += len(rows[i:i + 8])
-            if time.perf_counter() - t0 > seconds:
+        for t in ts:
+            s = int(np.searchsorted(cu, t, side="right") - 1)
+            a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+            tl = int(t) - a
+            c = tl // B
+            sc = mo.gate_scores_row(q[t], kbar[s], c)
+            idx, _, _ = mo.select_row(sc, c, topk)
+            J = mo.attended_tokens(idx, tl, B)
+            mo.attend_row(q[t], k[a:a + L], v[a:a + L], J, scale)
+            done += 1
+            pairs += len(J)
+            if time.perf_counter() - t0 > j["seconds"]:
                 break
-        elapsed = time.perf_counter() - t0
+        t_rows = time.perf_counter() - t0
     finally:
-        if ctx:
+        if ctx is not None:
             ctx.__exit__(None, None, None)
-    sampled = rows[1:1 + done]
-    pairs = 0
-    cu_np = np.asarray(cu)
-    for t in sampled[:, 0]:
-        s = int(np.searchsorted(cu_np, t, side="right") - 1)
-        tl = int(t - cu_np[s])
-        c = tl // w.block_size
-        pairs += (tl % w.block_size) + 1 + w.block_size * min(w.topk - 1, c)
+    return done, pairs, t_pool, t_rows
+
+
+def cpu_baseline(x, w, rows_target, seconds):
+    """The fp64 oracle on the host's cores: P = len(os.sched_getaffinity(0))
+    forked worker processes (capped at the head count and at the 16 cores a
+    one-GPU share of the host holds), worker i taking head
+    i: it pools the head's keys once and then runs seeded query rows through
+    the oracle's per-row steps for about `seconds`.  Rates are the summed
+    attended-pair flops (4d per pair) over the wall time of the row phase."""
+    import multiprocessing as mp
+    import numpy as np
+    P = max(1, min(len(os.sched_getaffinity(0)), 16, w.heads))
+    heads = list(range(P))
+    # host copies of the workers' heads only (bf16 values, exact in fp32)
+    _CPU_JOB.clear()
+    for n in ("q", "k", "v"):
+        _CPU_JOB[n] = {h: x[n][:, h, :].float().cpu().numpy() for h in heads}
+    _CPU_JOB.update(cu=np.asarray(x["cu_seqlens"], dtype=np.int64), B=w.block_size,
+                    topk=w.topk, scale=w.scale, index=w.index, rows=rows_target,
+                    seconds=seconds)
+    t0 = time.perf_counter()
+    # fork (no exec): the workers inherit the arrays and never touch the GPU
+    with mp.get_context("fork").Pool(P) as pool:
+        res = pool.map(_cpu_worker, heads)
+    wall = time.perf_counter() - t0
+    _CPU_JOB.clear()
+    done = sum(r[0] for r in res)
+    pairs = sum(r[1] for r in res)
+    t_pool = max(r[2] for r in res)
+    t_rows = max(r[3] for r in res)
     flops = 4.0 * w.head_dim * pairs
-    per_row_s = elapsed / max(done, 1)
+    per_row_s = t_rows * P / max(done, 1)  # one core's time per row
     return {
-        "value": flops / elapsed / 1e12,
+        "value": flops / t_rows / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": P,
         "kind": "oracle",
-        "sample": (f"{done} seeded query rows of head 0 of the {w.name} workload "
-                   f"(after the head's {T}-token key pooling, {t_first:.1f} s, done once); "
-                   f"fp64 NumPy, BLAS pinned to 1 thread"),
-        "seconds": elapsed,
+        "sample": (f"{done} seeded query rows over heads 0..{P - 1} of the {w.name} workload, "
+                   f"one head per worker process ({P} processes, BLAS 1 thread each); each "
+                   f"worker pools its head's keys once ({t_pool:.1f} s) and then runs rows "
+                   f"through the oracle's per-row steps for {seconds:.0f} s; fp64 NumPy"),
+        "seconds": t_rows,
+        "wall_seconds": wall,
+        "pool_seconds": t_pool,
         "per_row_ms": per_row_s * 1e3,
-        "extrapolated_layer_s": per_row_s * T * w.heads,
+        "extrapolated_layer_s": (t_pool * w.heads + per_row_s * w.total_tokens * w.heads) / P,
     }
 
 
@@ -234,16 +272,26 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     torch.cuda.synchronize()
     prof = moba.Profiler().attach()
     prof.reset()
+    # one event pair per step on the stream the library launches on, for the
+    # median and minimum next to the mean of the wall clock
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        ev[i][0].record()
         step()
+        ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    per_step = sorted(a.elapsed_time(b) for a, b in ev)
+    step_stats = {"mean_ms": ms_step, "median_ms": per_step[len(per_step) // 2],
+                  "min_ms": per_step[0], "max_ms": per_step[-1]}
     kern = prof.summary()
     prof.reset()
-    print(f"[bench] {w.name}: moba {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: moba {ms_step:.3f} ms/step (median {step_stats['median_ms']:.3f},"
+          f" min {step_stats['min_ms']:.3f})", file=sys.stderr, flush=True)
 
     # the library's own dense causal kernel on the same inputs
     del ws
@@ -274,7 +322,7 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
         del x, q, k, v
         x = None
         torch.cuda.empty_cache()
-    return x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths
+    return x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths, step_stats
 
 
 def measured_peaks(torch, moba, dev):
@@ -368,9 +416,10 @@ def main():
     ap.add_argument("--workload", default="1m")
     ap.add_argument("--dense-reps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="seeded query rows per worker (head), bounded by --cpu-seconds")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--also", default="32k,10m,1m:bwd,1m:minmax,1m:window,1m:sink1",
+    ap.add_argument("--also", default="8k,32k,varlen,10m,1m:bwd,1m:minmax,1m:window,1m:sink1",
                     help="comma-separated extra workloads reported under other_workloads "
                          "(ms/layer, TFLOP/s, dense, speedup); NAME:minmax uses the min/max "
                          "pooled gate, NAME:window or NAME:sinkN static routing, NAME:bwd the "
@@ -406,7 +455,7 @@ def main():
 
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
-    x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths = measure(
+    x, geom, ms_step, kern, dense_ms, rec_dense_stages, lengths, step_stats = measure(
         torch, inputs, moba, w, dev, args.steps, args.warmup, args.dense_reps, keep=True)
     H, d = w.heads, w.head_dim
     q = x["q"]
@@ -464,6 +513,7 @@ def main():
                    "block_size": w.block_size, "topk": w.topk,
                    "sparsity_last_query": 1 - w.topk * w.block_size / max(w.seqlens)},
         "ms_per_layer": ms_step,
+        "step_ms": step_stats,
         "attended_pairs": pairs,
         "dense_ms": dense_ms,
         "dense_tflops": (4.0 * d * dense_pairs(w.seqlens, H) / (dense_ms * 1e-3) / 1e12
@@ -522,9 +572,8 @@ def main():
         # extrapolated from the headline's measured dense rate per causal pair
         big = wo.total_tokens > (1 << 22)
         dense_reps_o = 2 if (args.dense_reps and wname != w.name and not big) else 0
-        _, _, ms_o2, kern_o, dense_o, _, _ = measure(torch, inputs, moba, wo, dev, steps_o,
-                                                     max(1, args.warmup), dense_reps_o,
-                                                     gate=gate)
+        _, _, ms_o2, kern_o, dense_o, _, _, stats_o = measure(
+            torch, inputs, moba, wo, dev, steps_o, max(1, args.warmup), dense_reps_o, gate=gate)
         if dense_o is None and wname == w.name:
             dense_o = dense_ms
         pairs_o, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
@@ -541,6 +590,7 @@ def main():
             "attn_hist_tflops": (4.0 * wo.head_dim * hist_o / (ms_ho / n_ho * 1e-3) / 1e12
                                  if n_ho else None),
             "ms_per_layer": ms_o2,
+            "step_ms": stats_o,
             "effective_tflops": 4.0 * wo.head_dim * pairs_o / (ms_o2 * 1e-3) / 1e12,
             "dense_ms": dense_o,
             "speedup_vs_dense": (dense_o / ms_o2) if dense_o else None,

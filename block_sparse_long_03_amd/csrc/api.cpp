@@ -2,6 +2,7 @@
 // order.  See include/moba.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -110,16 +111,30 @@ moba::Geo make_geo(const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_
   g.num_heads = num_heads;
   g.head_dim = head_dim;
   g.block_size = block_size;
+  g.head_lo = 0;
+  g.head_cnt = num_heads;
   return g;
 }
 
+// historical list entries and tiles of one pass over the heads of g's group
 long long hist_entries_bound(const moba::Geo& g, int topk) {
-  return (long long)g.total_tokens * g.num_heads * (topk - 1);
+  return (long long)g.total_tokens * g.head_cnt * (topk - 1);
 }
 
 long long hist_tiles_bound(const moba::Geo& g, int topk) {
-  return moba::hist_tiles_bound(g.total_tokens, g.total_blocks, g.num_heads, g.head_dim,
+  return moba::hist_tiles_bound(g.total_tokens, g.total_blocks, g.head_cnt, g.head_dim,
                                 g.block_size, topk);
+}
+
+// heads per pass of moba_attn_fwd: 0 or anything above num_heads means all
+int heads_per_pass(int num_heads, int head_chunk) {
+  return (head_chunk <= 0 || head_chunk > num_heads) ? num_heads : head_chunk;
+}
+
+// 32-bit limits of one pass: list entries (and their offsets), the tile
+// grid, and the packed entries token * topk + slot
+bool pass_fits_int32(const moba::Geo& g, int topk) {
+  return hist_tiles_bound(g, topk) < (1LL << 31) && hist_entries_bound(g, topk) < (1LL << 31);
 }
 
 }  // namespace
@@ -196,6 +211,77 @@ size_t dense_workspace_bytes(bool bf16, long long NB, long long H, long long D, 
 }
 
 }  // namespace moba
+
+namespace {
+
+// One pass of moba_attn_fwd over the heads of g's group: V staging, bucketing,
+// historical and own-block attention into the group's partials, merge into
+// out and lse.
+moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, const moba::Geo& g,
+                      int topk, const int32_t* block_idx, float softmax_scale, void* out,
+                      int out_dtype, float* lse, char* ws, const moba::AttnWorkspace& L,
+                      hipStream_t s) {
+  const long long tiles = hist_tiles_bound(g, topk);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* tile_offsets = (int32_t*)(ws + L.tile_offsets);
+  int32_t* list = (int32_t*)(ws + L.list);
+  float* lse_part = (float*)(ws + L.lse_part);
+  void* o_part = ws + L.o_part;
+  uint32_t* vmax = (uint32_t*)(ws + L.vmax);
+  const bool out_bf16 = out_dtype == MOBA_BF16;
+  hipError_t e;
+
+  if (bf16) {
+    uint16_t* vt = (uint16_t*)(ws + L.vt);
+    int4* tile_info = (int4*)(ws + L.tile_info);
+    if ((e = timed("v_stage", s, [&] { return moba::launch_v_transpose(v, g, vmax, vt, s); })) !=
+        hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("bucket", s, [&] {
+           return moba::launch_bucket(block_idx, g, topk,
+                                      moba::hist_tile_q(g.block_size, g.head_dim), counts,
+                                      offsets, tile_offsets, list, tile_info, tiles, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_hist", s, [&] {
+           return moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list,
+                                              tile_info, tiles, (uint16_t*)o_part, lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_own", s, [&] {
+           return moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale,
+                                             (uint16_t*)o_part, lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+  } else {
+    if ((e = timed("bucket", s, [&] {
+           return moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
+                                      tile_offsets, list, nullptr, 0, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_hist", s, [&] {
+           return moba::launch_attn_f32_hist((const float*)q, (const float*)k, (const float*)v,
+                                             g, topk, softmax_scale, list, offsets,
+                                             hist_entries_bound(g, topk), (float*)o_part,
+                                             lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = timed("attn_own", s, [&] {
+           return moba::launch_attn_f32_own((const float*)q, (const float*)k, (const float*)v,
+                                            g, topk, softmax_scale, (float*)o_part, lse_part, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+  }
+  if ((e = timed("merge", s, [&] {
+         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, vmax, out,
+                                   out_bf16, lse, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  return MOBA_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -314,13 +400,14 @@ moba_status moba_static_select(const int32_t* cu_seqlens, const int32_t* cu_bloc
 }
 
 size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks, int num_heads,
-                                 int head_dim, int block_size, int topk) {
+                                 int head_dim, int block_size, int topk, int head_chunk) {
   if (!dtype_ok(dtype) || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||
       (head_dim != 64 && head_dim != 128) || block_size < 64 || block_size % 64 != 0 ||
-      check_topk(total_tokens, topk) != MOBA_OK)
+      head_chunk < 0 || check_topk(total_tokens, topk) != MOBA_OK)
     return 0;
-  return moba::attn_workspace_layout(dtype == MOBA_BF16, total_tokens, total_blocks, num_heads,
-                                     head_dim, block_size, topk)
+  return moba::attn_workspace_layout(dtype == MOBA_BF16, total_tokens, total_blocks,
+                                     heads_per_pass(num_heads, head_chunk), head_dim,
+                                     block_size, topk)
       .total + kAlign;
 }
 
@@ -329,7 +416,8 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
                           int total_tokens, int max_seqlen, int total_blocks, int num_heads,
                           int head_dim, int block_size, int topk, const int32_t* block_idx,
                           float softmax_scale, void* out, int out_dtype, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          int head_chunk, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
                                   max_seqlen, total_blocks, num_heads, head_dim, block_size);
   if (st != MOBA_OK) return st;
@@ -337,77 +425,26 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
   if (st != MOBA_OK) return st;
   if (!dtype_ok(out_dtype)) return MOBA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MOBA_ERR_INVALID_ARG;
+  if (head_chunk < 0) return MOBA_ERR_INVALID_ARG;
+  const int hc = heads_per_pass(num_heads, head_chunk);
+  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
+                         total_blocks, num_heads, head_dim, block_size);
+  g.head_cnt = hc;
+  if (!pass_fits_int32(g, topk)) return MOBA_ERR_UNSUPPORTED;
   if (total_tokens == 0) return MOBA_OK;
   if (!q || !k || !v || !block_idx || !out || !lse || !workspace) return MOBA_ERR_INVALID_ARG;
   if ((uintptr_t)workspace % kAlign != 0) return MOBA_ERR_INVALID_ARG;
   const bool bf16 = dtype == MOBA_BF16;
   const moba::AttnWorkspace L = moba::attn_workspace_layout(
-      bf16, total_tokens, total_blocks, num_heads, head_dim, block_size, topk);
+      bf16, total_tokens, total_blocks, hc, head_dim, block_size, topk);
   if (workspace_bytes < L.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
-  moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
-                         total_blocks, num_heads, head_dim, block_size);
-  const long long tiles = hist_tiles_bound(g, topk);
-  if (tiles >= (1LL << 31) || hist_entries_bound(g, topk) / 4 >= (1LL << 31))
-    return MOBA_ERR_UNSUPPORTED;
-
-  char* ws = (char*)workspace;
-  int32_t* counts = (int32_t*)(ws + L.counts);
-  int32_t* offsets = (int32_t*)(ws + L.offsets);
-  int32_t* tile_offsets = (int32_t*)(ws + L.tile_offsets);
-  int32_t* list = (int32_t*)(ws + L.list);
-  float* lse_part = (float*)(ws + L.lse_part);
-  void* o_part = ws + L.o_part;
-  uint32_t* vmax = (uint32_t*)(ws + L.vmax);
-  hipStream_t s = (hipStream_t)stream;
-  const bool out_bf16 = out_dtype == MOBA_BF16;
-  hipError_t e;
-
-  if (bf16) {
-    uint16_t* vt = (uint16_t*)(ws + L.vt);
-    int4* tile_info = (int4*)(ws + L.tile_info);
-    if ((e = timed("v_stage", s, [&] { return moba::launch_v_transpose(v, g, vmax, vt, s); })) !=
-        hipSuccess)
-      return hip_fail(e);
-    if ((e = timed("bucket", s, [&] {
-           return moba::launch_bucket(block_idx, g, topk,
-                                      moba::hist_tile_q(g.block_size, g.head_dim), counts,
-                                      offsets, tile_offsets, list, tile_info, tiles, s);
-         })) != hipSuccess)
-      return hip_fail(e);
-    if ((e = timed("attn_hist", s, [&] {
-           return moba::launch_attn_mfma_hist(q, k, vt, g, topk, softmax_scale, list,
-                                              tile_info, tiles, (uint16_t*)o_part, lse_part, s);
-         })) != hipSuccess)
-      return hip_fail(e);
-    if ((e = timed("attn_own", s, [&] {
-           return moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale,
-                                             (uint16_t*)o_part, lse_part, s);
-         })) != hipSuccess)
-      return hip_fail(e);
-  } else {
-    if ((e = timed("bucket", s, [&] {
-           return moba::launch_bucket(block_idx, g, topk, moba::kF32TileQ, counts, offsets,
-                                      tile_offsets, list, nullptr, 0, s);
-         })) != hipSuccess)
-      return hip_fail(e);
-    if ((e = timed("attn_hist", s, [&] {
-           return moba::launch_attn_f32_hist((const float*)q, (const float*)k, (const float*)v,
-                                             g, topk, softmax_scale, list, offsets,
-                                             hist_entries_bound(g, topk), (float*)o_part,
-                                             lse_part, s);
-         })) != hipSuccess)
-      return hip_fail(e);
-    if ((e = timed("attn_own", s, [&] {
-           return moba::launch_attn_f32_own((const float*)q, (const float*)k, (const float*)v,
-                                            g, topk, softmax_scale, (float*)o_part, lse_part, s);
-         })) != hipSuccess)
-      return hip_fail(e);
+  for (int h0 = 0; h0 < num_heads; h0 += hc) {
+    g.head_lo = h0;
+    g.head_cnt = std::min(hc, num_heads - h0);
+    st = attn_pass(q, k, v, bf16, g, topk, block_idx, softmax_scale, out, out_dtype, lse,
+                   (char*)workspace, L, (hipStream_t)stream);
+    if (st != MOBA_OK) return st;
   }
-  if ((e = timed("merge", s, [&] {
-         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, vmax, out,
-                                   out_bf16, lse, s);
-       })) != hipSuccess)
-    return hip_fail(e);
   return MOBA_OK;
 }
 
@@ -445,7 +482,7 @@ moba_status moba_attn_bwd(const void* q, const void* k, const void* v, const voi
   const long long tiles = moba::bwd_tiles_bound(total_tokens, total_blocks, num_heads, topk);
   moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
                          total_blocks, num_heads, head_dim, block_size);
-  if (tiles >= (1LL << 31) || hist_entries_bound(g, topk) / 4 >= (1LL << 31))
+  if (tiles >= (1LL << 31) || hist_entries_bound(g, topk) >= (1LL << 31))
     return MOBA_ERR_UNSUPPORTED;
   char* ws = (char*)workspace;
   int32_t* counts = (int32_t*)(ws + L.counts);

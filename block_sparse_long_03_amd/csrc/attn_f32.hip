@@ -46,15 +46,17 @@ __device__ __forceinline__ void attend_range_f32(const float* __restrict__ q,
   if (lane == 0) *lse_out = m + logf(l);
 }
 
-// historical partials: one wave per list entry
+// historical partials: one wave per list entry.  Lists and partials cover the
+// HC heads h0 .. h0 + HC - 1 (indexed by the place in the group); q, k, v
+// rows have H heads.
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_hist_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
-    int num_seqs, int total_tokens, int H, int NB, int block_size, int topk, float scale,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ offsets,
+    int num_seqs, int total_tokens, int H, int h0, int HC, int NB, int block_size, int topk,
+    float scale, const int32_t* __restrict__ list, const int32_t* __restrict__ offsets,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
-  const int nkeys = H * NB;
+  const int nkeys = HC * NB;
   const long long e = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= offsets[nkeys]) return;
   const int key = upper_index(offsets, nkeys, (int)e);
@@ -67,23 +69,26 @@ __global__ __launch_bounds__(256) void attn_f32_hist_kernel(
   const int hi = min(lo + block_size, len);
   const int ent = list[e];
   const int t = ent / topk;
-  const size_t oi = ((size_t)t * H + h) * topk + (ent - t * topk);
-  attend_range_f32<D>(q, k, v, H, h, t, start, lo, hi, scale, o_part + oi * D, lse_part + oi);
+  const size_t oi = ((size_t)t * HC + h) * topk + (ent - t * topk);
+  attend_range_f32<D>(q, k, v, H, h0 + h, t, start, lo, hi, scale, o_part + oi * D,
+                      lse_part + oi);
 }
 
-// own-block partials (mode 0) or dense causal output (mode 1): one wave per row
+// own-block partials (mode 0, rows of the HC heads h0 .. h0 + HC - 1, partials
+// indexed by the place in the group) or dense causal output (mode 1, every
+// head: h0 = 0, HC = H): one wave per row
 template <int D, int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(256) void attn_f32_rows_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ cu_seqlens, int num_seqs, int total_tokens, int H,
-    int block_size, int topk, float scale, float* __restrict__ o_part,
+    const int32_t* __restrict__ cu_seqlens, int num_seqs, int total_tokens, int H, int h0,
+    int HC, int block_size, int topk, float scale, float* __restrict__ o_part,
     float* __restrict__ lse_part, void* __restrict__ out, float* __restrict__ lse) {
   __shared__ float obuf[4][D];
   const int wv = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * 4 + wv;
-  if (row >= (long long)total_tokens * H) return;
-  const int t = (int)(row / H);
-  const int h = (int)(row - (long long)t * H);
+  if (row >= (long long)total_tokens * HC) return;
+  const int t = (int)(row / HC);
+  const int h = h0 + (int)(row - (long long)t * HC);
   const int s = upper_index(cu_seqlens, num_seqs, t);
   const int start = cu_seqlens[s];
   const int p = t - start;
@@ -111,8 +116,9 @@ hipError_t launch_attn_f32_hist(const float* q, const float* k, const float* v, 
   dim3 grid((unsigned)((max_entries + 3) / 4));
 #define MOBA_F32H(D)                                                                      \
   hipLaunchKernelGGL(attn_f32_hist_kernel<D>, grid, dim3(256), 0, st, q, k, v, g.cu_seqlens, \
-                     g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads, g.total_blocks,  \
-                     g.block_size, topk, scale, list, offsets, o_part, lse_part)
+                     g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads, g.head_lo,       \
+                     g.head_cnt, g.total_blocks, g.block_size, topk, scale, list, offsets,  \
+                     o_part, lse_part)
   if (g.head_dim == 128) MOBA_F32H(128); else MOBA_F32H(64);
 #undef MOBA_F32H
   return hipGetLastError();
@@ -121,17 +127,19 @@ hipError_t launch_attn_f32_hist(const float* q, const float* k, const float* v, 
 hipError_t launch_attn_f32_own(const float* q, const float* k, const float* v, const Geo& g,
                                int topk, float scale, float* o_part, float* lse_part,
                                hipStream_t st) {
-  const long long rows = (long long)g.total_tokens * g.num_heads;
+  const long long rows = (long long)g.total_tokens * g.head_cnt;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 3) / 4));
   if (g.head_dim == 128)
     hipLaunchKernelGGL((attn_f32_rows_kernel<128, 0, false>), grid, dim3(256), 0, st, q, k, v,
-                       g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.block_size,
-                       topk, scale, o_part, lse_part, nullptr, nullptr);
+                       g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.head_lo,
+                       g.head_cnt, g.block_size, topk, scale, o_part, lse_part, nullptr,
+                       nullptr);
   else
     hipLaunchKernelGGL((attn_f32_rows_kernel<64, 0, false>), grid, dim3(256), 0, st, q, k, v,
-                       g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.block_size,
-                       topk, scale, o_part, lse_part, nullptr, nullptr);
+                       g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.head_lo,
+                       g.head_cnt, g.block_size, topk, scale, o_part, lse_part, nullptr,
+                       nullptr);
   return hipGetLastError();
 }
 
@@ -143,8 +151,8 @@ hipError_t launch_attn_f32_dense(const float* q, const float* k, const float* v,
   dim3 grid((unsigned)((rows + 3) / 4));
 #define MOBA_F32D(D, OB)                                                                   \
   hipLaunchKernelGGL((attn_f32_rows_kernel<D, 1, OB>), grid, dim3(256), 0, st, q, k, v,     \
-                     g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.block_size,   \
-                     1, scale, nullptr, nullptr, out, lse)
+                     g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, 0, g.num_heads, \
+                     g.block_size, 1, scale, nullptr, nullptr, out, lse)
   if (g.head_dim == 128) { if (out_bf16) MOBA_F32D(128, true); else MOBA_F32D(128, false); }
   else { if (out_bf16) MOBA_F32D(64, true); else MOBA_F32D(64, false); }
 #undef MOBA_F32D

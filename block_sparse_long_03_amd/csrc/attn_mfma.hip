@@ -61,13 +61,16 @@ struct MfmaArgs {
   const uint32_t* vmax_bits;   // per-head max |v| (fp32 bits): dense mode scales back
   const int32_t* cu_seqlens;
   const int32_t* cu_blocks;
-  int num_seqs, total_tokens, H, block_size, topk, NB;
+  // H: heads of the group this launch covers (the head index h below is a
+  // place in it; partials and staged V are laid out for H heads); Hs: heads
+  // of the q/k (and dense out/lse) rows; h0: global head of place 0
+  int num_seqs, total_tokens, H, Hs, h0, block_size, topk, NB;
   int tiles_per_unit;  // own: query tiles per block; dense: query tiles per sequence
   int units_per_seq;   // own: max blocks per sequence
   float scale2;        // softmax scale * log2(e)
   const int32_t* list;
   const int4* tile_info;  // hist: {key, first entry, end entry, 0} per tile, key < 0 past the end
-  void* o_out;  // hist/own: fp16 partials [T, H, topk, D] (V units); dense: out [T, H, D]
+  void* o_out;  // hist/own: fp16 partials [T, H, topk, D] (V units); dense: out [T, Hs, D]
   float* lse_out;
 };
 
@@ -79,9 +82,13 @@ __device__ __forceinline__ int swz(int row) {
   return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// Lazy rescaling: the running max used as the exponent base only moves when a
-// new score exceeds it by more than 2^8, so the O accumulators are rescaled
-// rarely; probabilities stay below 256 (exact in the final normalisation).
+// Lazy rescaling: the running max used as the exponent base of a query only
+// moves when one of its new scores exceeds it by more than 2^8, so the O
+// accumulators are rescaled rarely; probabilities stay below 256 (exact in
+// the final normalisation).  The decision is taken per query column (the two
+// lanes of a column agree), never per wave, so a query's rounding is the same
+// whichever queries share its wave and the forward is bitwise reproducible
+// even though the order of the bucket lists is not.
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D, int MODE, bool OUT_BF16, int kWaves>
@@ -165,9 +172,10 @@ void attn_mfma_kernel(MfmaArgs a) {
       qtok = seq_start + p;
       qpos = p;
       oidx = (MODE == kModeOwn) ? ((long long)qtok * a.H + h) * a.topk + (a.topk - 1)
-                                : (long long)qtok * a.H + h;
+                                : (long long)qtok * a.Hs + a.h0 + h;
     }
   }
+  const int hg = a.h0 + h;  // global head of the q/k rows
   // smallest query position of the wave: chunks past it need the causal mask
   int wq_min = qtok >= 0 ? qpos : 0x7fffffff;
   for (int o = 32; o >= 1; o >>= 1) wq_min = min(wq_min, __shfl_xor(wq_min, o));
@@ -176,7 +184,7 @@ void attn_mfma_kernel(MfmaArgs a) {
   bf16x8 qreg[KS];
   if (!RES) {
     const bool qv = qtok >= 0;
-    const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.H + h) * D + 8 * hf;
+    const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.Hs + hg) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
@@ -195,8 +203,8 @@ void attn_mfma_kernel(MfmaArgs a) {
   constexpr int VROWS_I = kWaves * 1024 / VRB;
   static_assert(KROWS_I % 16 == 0 && VROWS_I % 16 == 0, "uniform per-instruction offsets");
   const int nchunks = (key_hi - key_lo + kTK - 1) / kTK;
-  const size_t krow_bytes = (size_t)a.H * D * 2;
-  const char* kseq = (const char*)a.k + ((size_t)seq_start * a.H + h) * D * 2;
+  const size_t krow_bytes = (size_t)a.Hs * D * 2;
+  const char* kseq = (const char*)a.k + ((size_t)seq_start * a.Hs + hg) * D * 2;
   const int krow0 = (w * 1024 + lane * 16) / KRB;
   const uint32_t koff0 = (uint32_t)(krow0 * krow_bytes +
                                     ((((lane * 16) % KRB) >> 4) ^ swz<KRB>(krow0)) * 16);
@@ -376,7 +384,9 @@ void attn_mfma_kernel(MfmaArgs a) {
     }
     fence();
     const float cand = max_with_partner(mx);  // in units of t: max(s) * scale2 - base_old
-    if (__ballot(cand > (m_use == -INFINITY ? -INFINITY : kRescaleSlack)) != 0) {
+    // per query column: a column's base moves only on its own scores, so its
+    // result does not depend on which other queries share the wave
+    if (cand > (m_use == -INFINITY ? -INFINITY : kRescaleSlack)) {
       const float m_new = fmaxf(m_use, base_old + cand);
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
       const float delta = (m_new == -INFINITY ? 0.f : m_new) - base_old;
@@ -506,7 +516,7 @@ void attn_mfma_kernel(MfmaArgs a) {
       }
       {
         const bool qv = qtok >= 0;
-        const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.H + h) * D + 8 * hf;
+        const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.Hs + hg) * D + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           u32x4 wv = {0u, 0u, 0u, 0u};
@@ -563,7 +573,9 @@ static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, cons
   a.cu_blocks = g.cu_blocks;
   a.num_seqs = g.num_seqs;
   a.total_tokens = g.total_tokens;
-  a.H = g.num_heads;
+  a.H = g.head_cnt;
+  a.Hs = g.num_heads;
+  a.h0 = g.head_lo;
   a.block_size = g.block_size;
   a.topk = topk;
   a.NB = g.total_blocks;
@@ -617,7 +629,7 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
   a.units_per_seq = (g.max_seqlen + g.block_size - 1) / g.block_size;
   a.o_out = o_part;
   a.lse_out = lse_part;
-  dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.num_heads);
+  dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit * a.units_per_seq), g.head_cnt);
   if (g.head_dim == 128) launch_mfma<128, kModeOwn, true>(waves, grid, st, a);
   else launch_mfma<64, kModeOwn, true>(waves, grid, st, a);
   return hipGetLastError();
@@ -634,7 +646,7 @@ hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* 
   a.units_per_seq = 1;
   a.o_out = out;
   a.lse_out = lse;
-  dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.num_heads);
+  dim3 grid((unsigned)(g.num_seqs * a.tiles_per_unit), g.head_cnt);
   if (g.head_dim == 128) {
     if (out_bf16) launch_mfma<128, kModeDense, true>(waves, grid, st, a);
     else launch_mfma<128, kModeDense, false>(waves, grid, st, a);

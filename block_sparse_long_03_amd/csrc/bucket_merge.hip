@@ -17,9 +17,10 @@ constexpr int kBucketTokensMax = 256;  // tokens per workgroup in count/scatter 
 constexpr int kBucketLdsBins = 8192;  // LDS histogram limit (heads x past blocks per tile)
 
 // Per (sequence tile of `tile_tokens` tokens): every (token, head) row of
-// block_idx, read in memory order (consecutive lanes take consecutive rows,
-// so a wave reads one contiguous range), counted into an LDS histogram per
-// (head, past block) and flushed with one global atomic per touched bin.
+// block_idx for the HC heads h0 .. h0 + HC - 1 of the group, read in memory
+// order (consecutive lanes take consecutive rows, so a wave reads one
+// contiguous range per token), counted into an LDS histogram per (head of the
+// group, past block) and flushed with one global atomic per touched bin.
 // The scatter pass reserves a range per bin, then places each entry: the
 // global token times slot_stride plus its slot, or (slot_stride 0) the token
 // alone.
@@ -27,7 +28,8 @@ template <bool kScatter>
 __global__ __launch_bounds__(256) void bucket_pass_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int tile_tokens,
-    int H, int NB, int block_size, int topk, int slot_stride, int32_t* __restrict__ counts,
+    int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
+    int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ list) {
   __shared__ int32_t hist[kBucketLdsBins];
   __shared__ int32_t basev[kScatter ? kBucketLdsBins : 1];
@@ -40,21 +42,21 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
   const int p1 = min(len, p0 + tile_tokens);
   const int nbins = (p1 - 1) / block_size;  // past blocks of the last row
   const int gb0 = cu_blocks[sid];
-  const bool use_lds = nbins * H <= kBucketLdsBins;
-  const int nrows = (p1 - p0) * H;
-  const int32_t* rows = block_idx + ((size_t)(start + p0) * H) * topk;
+  const bool use_lds = nbins * HC <= kBucketLdsBins;
+  const int nrows = (p1 - p0) * HC;
 
   if (use_lds) {
-    for (int b = threadIdx.x; b < nbins * H; b += 256) hist[b] = 0;
+    for (int b = threadIdx.x; b < nbins * HC; b += 256) hist[b] = 0;
     __syncthreads();
   }
-  // walks row r = (p - p0) * H + h, calling f(h, e, slot) for each accepted
-  // historical entry (0 <= e < c, increasing, inside the batch's blocks)
+  // walks row r = (p - p0) * HC + h of the group (head h0 + h), calling
+  // f(h, e, slot, p) for each accepted historical entry (0 <= e < c,
+  // increasing, inside the batch's blocks)
   auto walk = [&](int r, auto&& f) {
-    const int p = p0 + r / H;
-    const int h = r - (r / H) * H;
+    const int p = p0 + r / HC;
+    const int h = r - (r / HC) * HC;
     const int c = p / block_size;
-    const int32_t* row = rows + (size_t)r * topk;
+    const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * topk;
     int last = -1, nh = 0;
     auto visit = [&](int e) {
       if (e >= 0 && e < c && e > last) {
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
       });
     if (!use_lds) return;
     __syncthreads();
-    for (int b = threadIdx.x; b < nbins * H; b += 256) {
+    for (int b = threadIdx.x; b < nbins * HC; b += 256) {
       const int h = b / nbins, e = b - (b / nbins) * nbins;
       if (hist[b]) atomicAdd(&counts[(size_t)h * NB + gb0 + e], hist[b]);
     }
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
     walk(r, [&](int h, int e, int, int) { atomicAdd(&hist[h * nbins + e], 1); });
   __syncthreads();
   // reserve a range per touched bin, then place every entry
-  for (int b = threadIdx.x; b < nbins * H; b += 256) {
+  for (int b = threadIdx.x; b < nbins * HC; b += 256) {
     const int h = b / nbins, e = b - (b / nbins) * nbins;
     const int n = hist[b];
     const size_t key = (size_t)h * NB + gb0 + e;
@@ -180,7 +182,7 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
                          int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st,
                          bool tokens_only) {
   const int slot_stride = tokens_only ? 0 : topk;
-  const int n = g.num_heads * g.total_blocks;
+  const int n = g.head_cnt * g.total_blocks;
   if (n > 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
                        counts, n);
@@ -193,13 +195,15 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<false>), grid, dim3(256), 0, st, block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.total_blocks, g.block_size, topk, slot_stride, counts, offsets, list);
+                       g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk, slot_stride,
+                       counts, offsets, list);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, st, counts, n, tile_q,
                      offsets, tile_offsets);
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL((bucket_pass_kernel<true>), grid, dim3(256), 0, st, block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.total_blocks, g.block_size, topk, slot_stride, counts, offsets, list);
+                       g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk, slot_stride,
+                       counts, offsets, list);
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
                        st, offsets, tile_offsets, n, tile_q, max_tiles, tile_info);
@@ -220,9 +224,9 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v,
                                                    int total_tokens, int hd, int head_dim,
-                                                   uint32_t* __restrict__ vmax_bits) {
+                                                   int h0, uint32_t* __restrict__ vmax_bits) {
   __shared__ uint32_t red[256];
-  const int col0 = blockIdx.y * 64;          // 64 columns of one head
+  const int col0 = h0 * head_dim + blockIdx.y * 64;  // 64 columns of one head
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
   const int t0 = blockIdx.x * 2048;
   uint32_t m = 0u;
@@ -240,15 +244,16 @@ __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ 
     if (threadIdx.x < st) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + st]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) atomicMax(&vmax_bits[col0 / head_dim], red[0]);
+  if (threadIdx.x == 0) atomicMax(&vmax_bits[col0 / head_dim - h0], red[0]);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void v_transpose_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int H,
+    const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int H, int h0,
     int block_size, const uint32_t* __restrict__ vmax_bits, uint16_t* __restrict__ vt) {
   __shared__ float tile[64][D + 1];
+  const int HC = gridDim.y;  // heads of the group; h below is the place in it
   const int chunks_per_block = block_size / 64;
   const int gb = blockIdx.x / chunks_per_block;
   const int ci = blockIdx.x % chunks_per_block;
@@ -263,7 +268,8 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
   for (int i = threadIdx.x; i < 64 * SEG; i += 256) {
     const int r = i / SEG, c = i % SEG;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (r < nk) w = *reinterpret_cast<const u32x4*>(v + ((size_t)(start + local + r) * H + h) * D + c * 8);
+    if (r < nk)
+      w = *reinterpret_cast<const u32x4*>(v + ((size_t)(start + local + r) * H + h0 + h) * D + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       tile[r][c * 8 + 2 * e] = lo_bf16(w[e]) * scale;
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
     }
   }
   __syncthreads();
-  uint16_t* dst = vt + ((size_t)gb * H + h) * D * (size_t)block_size + ci * 64;
+  uint16_t* dst = vt + ((size_t)gb * HC + h) * D * (size_t)block_size + ci * 64;
   for (int i = threadIdx.x; i < D * 8; i += 256) {
     const int e = i / 8, seg = i % 8;  // 8 storage positions per thread
     uint32_t packed[4];
@@ -297,18 +303,20 @@ hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, 
   if (g.total_blocks == 0) return hipSuccess;
   const int hd = g.num_heads * g.head_dim;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, st, (int32_t*)vmax_bits,
-                     g.num_heads);
-  hipLaunchKernelGGL(vmax_kernel, dim3((g.total_tokens + 2047) / 2048, hd / 64), dim3(256), 0, st,
-                     (const uint16_t*)v, g.total_tokens, hd, g.head_dim, vmax_bits);
-  dim3 grid(g.total_blocks * (g.block_size / 64), g.num_heads);
+                     g.head_cnt);
+  hipLaunchKernelGGL(vmax_kernel,
+                     dim3((g.total_tokens + 2047) / 2048, g.head_cnt * g.head_dim / 64),
+                     dim3(256), 0, st, (const uint16_t*)v, g.total_tokens, hd, g.head_dim,
+                     g.head_lo, vmax_bits);
+  dim3 grid(g.total_blocks * (g.block_size / 64), g.head_cnt);
   if (g.head_dim == 128)
     hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)v,
                        g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads,
-                       g.block_size, vmax_bits, vt);
+                       g.head_lo, g.block_size, vmax_bits, vt);
   else
     hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, st, (const uint16_t*)v,
                        g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, g.num_heads,
-                       g.block_size, vmax_bits, vt);
+                       g.head_lo, g.block_size, vmax_bits, vt);
   return hipGetLastError();
 }
 
@@ -316,12 +324,14 @@ hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, 
 // merge: 16 lanes per (token, head) row, 16 rows per workgroup.  Each lane
 // owns D/16 consecutive output dims; the part weights exp(lse_p - lse) go
 // through LDS so that every lane can stream its slice of all the parts with
-// several loads in flight.
+// several loads in flight.  Rows are those of the HC heads h0 .. h0 + HC - 1:
+// partials and V scales are indexed by the head's place in that group,
+// block_idx, out and lse by its global head.
 // ---------------------------------------------------------------------------
 template <int D, bool kPartF16, bool kOutBf16>
 __global__ __launch_bounds__(256) void merge_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
-    int num_seqs, int total_tokens, int H, int block_size, int topk,
+    int num_seqs, int total_tokens, int H, int h0, int HC, int block_size, int topk,
     const void* __restrict__ o_part, const float* __restrict__ lse_part,
     const uint32_t* __restrict__ vmax_bits, void* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 16;  // output dims per lane
@@ -329,15 +339,17 @@ __global__ __launch_bounds__(256) void merge_kernel(
   __shared__ int slots[16][64];
   const int r16 = threadIdx.x >> 4;  // row within the workgroup
   const int li = threadIdx.x & 15;   // lane within the row
-  const long long row = (long long)blockIdx.x * 16 + r16;
-  const bool valid = row < (long long)total_tokens * H;
+  const long long row = (long long)blockIdx.x * 16 + r16;  // (token, head of the group)
+  const bool valid = row < (long long)total_tokens * HC;
+  const int t = (int)(row / HC);
+  const int hl = (int)(row - (long long)t * HC);
+  const long long grow = (long long)t * H + h0 + hl;       // (token, global head)
   int nparts = 0;
   float tot = 0.f;
   if (valid) {
-    const int t = (int)(row / H);
     const int s = upper_index(cu_seqlens, num_seqs, t);
     const int c = (t - cu_seqlens[s]) / block_size;
-    const int nh = count_hist(block_idx + row * topk, topk, c);
+    const int nh = count_hist(block_idx + grow * topk, topk, c);
     nparts = nh + 1;
     // part i < nh lives in slot i; the own block in slot topk - 1
     float l4[4];
@@ -421,11 +433,11 @@ __global__ __launch_bounds__(256) void merge_kernel(
   }
   if (kPartF16) {
     // fp16 partials are in units of 2^-e_h (the staged V's scale)
-    const float sc = __builtin_ldexpf(1.0f, v_exponent(vmax_bits[row % H]));
+    const float sc = __builtin_ldexpf(1.0f, v_exponent(vmax_bits[hl]));
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] *= sc;
   }
-  const size_t ob = (size_t)row * D + li * PER;
+  const size_t ob = (size_t)grow * D + li * PER;
   if (kOutBf16) {
     uint32_t* o = (uint32_t*)((uint16_t*)out + ob);
 #pragma unroll
@@ -438,19 +450,19 @@ __global__ __launch_bounds__(256) void merge_kernel(
       *reinterpret_cast<f32x4*>(o + e) = f4;
     }
   }
-  if (li == 0) lse[row] = tot;
+  if (li == 0) lse[grow] = tot;
 }
 
 hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
                         bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
                         void* out, bool out_bf16, float* lse, hipStream_t st) {
-  const long long rows = (long long)g.total_tokens * g.num_heads;
+  const long long rows = (long long)g.total_tokens * g.head_cnt;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
 #define MOBA_MERGE(D, PB, OB)                                                            \
   hipLaunchKernelGGL((merge_kernel<D, PB, OB>), grid, dim3(256), 0, st, block_idx,       \
-                     g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.block_size, \
-                     topk, o_part, lse_part, vmax_bits, out, lse)
+                     g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.head_lo,    \
+                     g.head_cnt, g.block_size, topk, o_part, lse_part, vmax_bits, out, lse)
   if (g.head_dim == 128) {
     if (part_f16) { if (out_bf16) MOBA_MERGE(128, true, true); else MOBA_MERGE(128, true, false); }
     else { if (out_bf16) MOBA_MERGE(128, false, true); else MOBA_MERGE(128, false, false); }

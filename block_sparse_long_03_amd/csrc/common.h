@@ -67,12 +67,20 @@ __device__ __forceinline__ float hi_f16(uint32_t w) {
 }
 
 // V is staged in fp16 for the PV products, scaled per head by 2^-e so that
-// the head's largest |v| stays below 2^15.  vmax_bits is the fp32 bit
-// pattern of that largest |v| (bf16 values convert exactly, only the scale
-// moves); e = 0 for any head whose values are below 32768.
+// the head's largest |v| lands in [2^14, 2^15), whatever the head's
+// magnitude: small heads are scaled up, large ones down.  The largest staged
+// value then stays below the fp16 limit, and every value of at least 2^-28
+// times the head's largest is a normal fp16 number.  The scale is a power of
+// two and fp16 carries more significand bits than bf16, so such a value
+// converts exactly; smaller ones round to fp16 subnormals (their share of any
+// output is below 2^-28 of the head's scale).  vmax_bits is the fp32 bit
+// pattern of the head's largest |v|, and vmax < 2^x with x from its exponent
+// field.  e is clamped at -126 so that 2^-e stays a finite fp32 number: a
+// head of zeros, or one whose largest value is subnormal, takes the largest
+// scale-up.
 __device__ __forceinline__ int v_exponent(uint32_t vmax_bits) {
   const int x = (int)((vmax_bits >> 23) & 0xffu) - 126;  // vmax < 2^x
-  return max(0, x - 15);
+  return max(-126, x - 15);
 }
 
 // Index of the sequence that owns global block `gb` (largest s with

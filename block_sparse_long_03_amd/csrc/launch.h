@@ -8,6 +8,11 @@
 
 namespace moba {
 
+// num_heads is the head count of the [T, H, d] tensors (their row stride in
+// heads).  A forward pass may run over one group of heads at a time:
+// head_lo and head_cnt name the group, whose workspace arrays (partials,
+// lists, staged V) are laid out for head_cnt heads and indexed by the head's
+// place in the group.  Calls over all heads use head_lo 0, head_cnt num_heads.
 struct Geo {
   const int32_t* cu_seqlens;
   const int32_t* cu_blocks;
@@ -18,6 +23,8 @@ struct Geo {
   int num_heads;
   int head_dim;
   int block_size;
+  int head_lo;
+  int head_cnt;
 };
 
 // Waves per workgroup of the MFMA attention kernels, one 32-query column

@@ -27,7 +27,7 @@ MOBA_ERR_HIP = -4
 MOBA_F32 = 0
 MOBA_BF16 = 1
 # the MOBA_API_VERSION of include/moba.h these bindings are written for
-API_VERSION = 2
+API_VERSION = 3
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
@@ -77,9 +77,10 @@ def lib():
     L.moba_static_select.restype = i32
     L.moba_static_select.argtypes = [vp, vp] + [i32] * 8 + [vp, vp]
     L.moba_attn_workspace_bytes.restype = sz
-    L.moba_attn_workspace_bytes.argtypes = [i32] * 7
+    L.moba_attn_workspace_bytes.argtypes = [i32] * 8
     L.moba_attn_fwd.restype = i32
-    L.moba_attn_fwd.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, vp, sz, vp]
+    L.moba_attn_fwd.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, i32, vp, sz,
+                                                          vp]
     L.moba_attn_bwd_workspace_bytes.restype = sz
     L.moba_attn_bwd_workspace_bytes.argtypes = [i32] * 7
     L.moba_attn_bwd.restype = i32
@@ -231,9 +232,10 @@ def moba_static_select(geom, num_heads, topk, sink_blocks, block_idx=None, devic
 
 
 def moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
-                              block_size, topk):
+                              block_size, topk, head_chunk=0):
+    """Workspace of moba_attn_fwd for passes of head_chunk heads (0: all)."""
     return int(lib().moba_attn_workspace_bytes(dtype, total_tokens, total_blocks, num_heads,
-                                               head_dim, block_size, topk))
+                                               head_dim, block_size, topk, int(head_chunk)))
 
 
 def moba_attn_bwd_workspace_bytes(dtype, total_tokens, total_blocks, num_heads, head_dim,
@@ -254,7 +256,9 @@ def _workspace(nbytes, device):
 
 
 def moba_attn_fwd(q, k, v, geom, topk, block_idx, scale, out=None, out_dtype=None, lse=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, head_chunk=0):
+    """Sparse attention over the selected blocks; head_chunk heads per pass
+    (0: all heads in one pass; the workspace scales with it)."""
     H, d = _qkv_shape(q, geom)
     dt = _dtype_code(q.dtype)
     out_dtype = q.dtype if out_dtype is None else out_dtype
@@ -264,11 +268,12 @@ def moba_attn_fwd(q, k, v, geom, topk, block_idx, scale, out=None, out_dtype=Non
         lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = _workspace(moba_attn_workspace_bytes(
-            dt, geom.total_tokens, geom.total_blocks, H, d, geom.block_size, topk), q.device)
+            dt, geom.total_tokens, geom.total_blocks, H, d, geom.block_size, topk, head_chunk),
+            q.device)
     _check("moba_attn_fwd", lib().moba_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), dt, *geom.args(H, d), int(topk), _ptr(block_idx),
-        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), int(head_chunk),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 
@@ -330,13 +335,14 @@ class Profiler:
             self.handle = None
 
 
-def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):
+def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None,
+            head_chunk=0):
     """MoBA prefill forward: pool -> gate/top-k -> sparse attention.
     Returns (out, lse, block_idx)."""
     kbar = moba_pool_keys(k, geom, stream=stream)
     idx = moba_gate_topk(q, kbar, geom, topk, stream=stream)
     out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
-                             workspace=workspace, stream=stream)
+                             workspace=workspace, stream=stream, head_chunk=head_chunk)
     return out, lse, idx
 
 

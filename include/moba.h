@@ -34,7 +34,11 @@
  *     production path: bf16 MFMA, fp32 accumulation) or MOBA_F32 (fp32 VALU
  *     path for small, high-precision checks).
  *   - Supported: head_dim 64 or 128; block_size a positive multiple of 64;
- *     1 <= topk <= 64; total_tokens * topk < 2^31.
+ *     1 <= topk <= 64; total_tokens * topk < 2^31.  The query lists of the
+ *     attention calls hold 32-bit offsets, so moba_attn_fwd also needs
+ *     total_tokens * heads per pass * (topk - 1) < 2^31 (see head_chunk) and
+ *     moba_attn_bwd total_tokens * num_heads * (topk - 1) < 2^31; a larger
+ *     geometry returns MOBA_ERR_UNSUPPORTED before anything is launched.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream), allocates no device memory and keeps no state between
  *     calls.  Arguments are validated on the host before anything is
@@ -53,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOBA_API_VERSION 2
+#define MOBA_API_VERSION 3
 
 typedef enum moba_status {
   MOBA_OK = 0,
@@ -175,14 +179,17 @@ moba_status moba_static_select(const int32_t* cu_seqlens, const int32_t* cu_bloc
                                int sink_blocks, int32_t* block_idx, void* stream);
 
 /*
- * Workspace bytes moba_attn_fwd needs for this geometry (0 when the
- * arguments are invalid).  The workspace holds the per-(KV block, head)
- * query lists, the per-(query, selected block) partial results and a
- * transposed copy of V.
+ * Workspace bytes moba_attn_fwd needs for this geometry and head_chunk (0
+ * when the arguments are invalid).  The workspace holds, for the heads of one
+ * pass, the per-(KV block, head) query lists, the per-(query, selected block)
+ * partial results and a transposed copy of V, so it scales with head_chunk:
+ * about total_tokens * heads per pass * topk * (2 head_dim + 8) bytes.
+ *   head_chunk  heads per pass of moba_attn_fwd; 0, or any value of at least
+ *               num_heads, means all heads in one pass; negative is invalid
  */
 size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks,
                                  int num_heads, int head_dim, int block_size,
-                                 int topk);
+                                 int topk, int head_chunk);
 
 /*
  * Sparse attention over the selected blocks.
@@ -201,9 +208,21 @@ size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks,
  *              ignored; the own block is always attended.
  *   out        [total_tokens, num_heads, head_dim], out_dtype (F32 or BF16)
  *   lse        [total_tokens, num_heads] fp32, natural log
- *   workspace  device buffer of at least moba_attn_workspace_bytes(...)
- *              bytes, 256-byte aligned; its contents on entry are ignored
- * Results are deterministic (no floating-point atomics).
+ *   head_chunk heads per pass (0 or >= num_heads: all heads at once).  The
+ *              heads are processed in consecutive groups of head_chunk, one
+ *              after the other on `stream`, each group reusing the same
+ *              workspace; the results do not depend on head_chunk.  Heads
+ *              are independent in MoBA, which is what lets a layer too large
+ *              for one workspace run head group by head group ("MoBA:
+ *              Learned Block Sparsity for Long-Context Attention",
+ *              "Efficiency and Implementation": the 10M-token run splits the
+ *              work at the level of query heads).
+ *   workspace  device buffer of at least moba_attn_workspace_bytes(...,
+ *              head_chunk) bytes, 256-byte aligned; its contents on entry
+ *              are ignored
+ * Results are bitwise reproducible: no floating-point atomics, and each
+ * query's arithmetic depends only on its own data and its selected blocks,
+ * not on the (scheduling-dependent) order of the query lists.
  */
 moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                           const int32_t* cu_seqlens, const int32_t* cu_blocks,
@@ -211,8 +230,8 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
                           int total_blocks, int num_heads, int head_dim,
                           int block_size, int topk, const int32_t* block_idx,
                           float softmax_scale, void* out, int out_dtype,
-                          float* lse, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          float* lse, int head_chunk, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Backward of moba_attn_fwd: gradients of out with respect to q, k and v for
@@ -272,24 +291,6 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
                                   size_t workspace_bytes, void* stream);
 
 /*
- * Measurement support (not part of the computation).
- * A profiler attached to the calling thread brackets every kernel launch the
- * library makes from that thread with a pair of HIP events on the launch's
- * stream and accumulates, per kernel name, the number of launches and their
- * total duration.  The profiler owns its events (host-side HIP objects; no
- * device memory); the results of the computation do not depend on it.
- *   moba_profiler_create   returns a new profiler in *out
- *   moba_profiler_attach   attaches p to the calling thread (NULL detaches)
- *   moba_profiler_reset    forgets all recorded launches
- *   moba_profiler_read     waits for the recorded events and returns the
- *                          launches and total milliseconds of kernel `name`
- *                          (0 and 0.0 if it never ran); names are the
- *                          kernels' short names, e.g. "attn_hist"
- *   moba_profiler_names    writes the distinct kernel names seen so far as a
- *                          comma-separated list into buf (truncated to len)
- *   moba_profiler_destroy  frees p (detach it first)
- */
-/*
  * Measurement support (not part of the computation): sustained bf16 MFMA
  * rate probes.  Launches `workgroups` workgroups of 4 waves; every wave runs
  * 4 independent chains of `iterations` v_mfma_f32_32x32x16_bf16, i.e.
@@ -310,6 +311,24 @@ moba_status moba_dense_causal_fwd(const void* q, const void* k, const void* v, i
 moba_status moba_probe_mfma_rate(int workgroups, int iterations, int operands, float* sink,
                                  void* stream);
 
+/*
+ * Measurement support (not part of the computation).
+ * A profiler attached to the calling thread brackets every kernel launch the
+ * library makes from that thread with a pair of HIP events on the launch's
+ * stream and accumulates, per kernel name, the number of launches and their
+ * total duration.  The profiler owns its events (host-side HIP objects; no
+ * device memory); the results of the computation do not depend on it.
+ *   moba_profiler_create   returns a new profiler in *out
+ *   moba_profiler_attach   attaches p to the calling thread (NULL detaches)
+ *   moba_profiler_reset    forgets all recorded launches
+ *   moba_profiler_read     waits for the recorded events and returns the
+ *                          launches and total milliseconds of kernel `name`
+ *                          (0 and 0.0 if it never ran); names are the
+ *                          kernels' short names, e.g. "attn_hist"
+ *   moba_profiler_names    writes the distinct kernel names seen so far as a
+ *                          comma-separated list into buf (truncated to len)
+ *   moba_profiler_destroy  frees p (detach it first)
+ */
 typedef struct moba_profiler moba_profiler;
 moba_status moba_profiler_create(moba_profiler** out);
 moba_status moba_profiler_attach(moba_profiler* p);

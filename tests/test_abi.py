@@ -57,11 +57,20 @@ def pool(L, **kw):
                             kw.get("kbar", FAKE), None)
 
 
-def attn(L, topk=3, scale=0.1, ws=FAKE, ws_bytes=1 << 40, out_dtype=1, **kw):
+def attn(L, topk=3, scale=0.1, ws=FAKE, ws_bytes=1 << 40, out_dtype=1, head_chunk=0, **kw):
     g = dict(GEO, **kw)
     return L.moba_attn_fwd(FAKE, FAKE, FAKE, kw.get("dtype", 1), g["cu"], g["cb"], g["S"],
                            g["T"], g["maxL"], g["NB"], g["H"], g["d"], g["B"], topk, FAKE,
-                           ctypes.c_float(scale), FAKE, out_dtype, FAKE, ws, ws_bytes, None)
+                           ctypes.c_float(scale), FAKE, out_dtype, FAKE, head_chunk, ws,
+                           ws_bytes, None)
+
+
+def bwd(L, topk=3, ws_bytes=1, **kw):
+    # the 1-byte workspace stops every valid call before a launch
+    g = dict(GEO, **kw)
+    return L.moba_attn_bwd(FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, g["cu"], g["cb"], g["S"],
+                           g["T"], g["maxL"], g["NB"], g["H"], g["d"], g["B"], topk, FAKE,
+                           ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
 
 
 def test_invalid_arguments(L):
@@ -82,6 +91,7 @@ def test_invalid_arguments(L):
     assert attn(L, out_dtype=5) == E
     assert attn(L, ws=None) == E
     assert attn(L, ws=ctypes.c_void_p(0x10010)) == E   # not 256-byte aligned
+    assert attn(L, head_chunk=-1) == E
 
 
 def static(L, topk=3, sink=1, idx=FAKE, **kw):
@@ -140,8 +150,40 @@ def test_unsupported(L):
     assert attn(L, topk=65) == U
 
 
+# T = 2^20, H = 40, d 64, B 4096, k 64: T * k < 2^31, but the query lists of
+# all heads would hold T * H * (k - 1) = 2.6e9 entries, past their int32
+# offsets
+BIG = dict(T=1 << 20, maxL=1 << 20, NB=256, H=40, d=64, B=4096)
+
+
+def test_list_offsets_must_fit_int32(L):
+    U = moba.MOBA_ERR_UNSUPPORTED
+    assert (1 << 20) * 64 < (1 << 31) <= (1 << 20) * 40 * 63
+    assert bwd(L, topk=64, ws_bytes=1 << 60, **BIG) == U
+    assert attn(L, topk=64, **BIG) == U                  # all heads in one pass
+    assert attn(L, topk=64, head_chunk=40, **BIG) == U
+    # passes of 8 heads hold 5.3e8 entries each: accepted (the fake workspace
+    # of 1 byte is then too small, which is checked afterwards)
+    assert attn(L, topk=64, head_chunk=8, ws_bytes=1, **BIG) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(L, topk=32, **dict(BIG, H=4)) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_head_chunk_workspace(L):
+    full = L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, 0)
+    assert full == L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, 4)
+    assert full == L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, 99)
+    one = L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, 1)
+    two = L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, 2)
+    assert 0 < one < two < full
+    # the partials of one head: T * k * d fp16
+    assert one >= 1000 * 3 * 128 * 2 and full >= 4 * 1000 * 3 * 128 * 2
+    assert L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, -1) == 0
+    # a workspace sized for passes of one head is too small for all heads at once
+    assert attn(L, ws_bytes=one, H=4) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_workspace_too_small(L):
-    need = L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 3)
+    need = L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 3, 0)
     assert need > 0
     assert attn(L, ws_bytes=need // 2) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
     dneed = L.moba_dense_workspace_bytes(1, 1000, 8, 2, 128, 128)
@@ -151,11 +193,11 @@ def test_workspace_too_small(L):
 
 
 def test_workspace_sizes(L):
-    assert L.moba_attn_workspace_bytes(1, 1000, 8, 2, 96, 128, 3) == 0
-    assert L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 0) == 0
-    a = L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 3)
-    b = L.moba_attn_workspace_bytes(1, 2000, 16, 2, 128, 128, 3)
-    f = L.moba_attn_workspace_bytes(0, 1000, 8, 2, 128, 128, 3)
+    assert L.moba_attn_workspace_bytes(1, 1000, 8, 2, 96, 128, 3, 0) == 0
+    assert L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 0, 0) == 0
+    a = L.moba_attn_workspace_bytes(1, 1000, 8, 2, 128, 128, 3, 0)
+    b = L.moba_attn_workspace_bytes(1, 2000, 16, 2, 128, 128, 3, 0)
+    f = L.moba_attn_workspace_bytes(0, 1000, 8, 2, 128, 128, 3, 0)
     assert b > a > 0 and f > 0
     # the o partials dominate: T * H * k * d elements
     assert a >= 1000 * 2 * 3 * 128 * 2

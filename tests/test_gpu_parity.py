@@ -140,18 +140,25 @@ def test_moba_sampled(dev, name, per_head, heads):
 
 def test_moba_1m_sampled(dev):
     """The 1M-token workload in the launch configuration bench.py times:
-    outputs on 512 seeded rows (4 heads), selections on every row of one
-    head, and causal validity of every selection row."""
+    outputs on 1024 seeded rows (8 heads), selections on every row of two
+    heads, and causal validity of every selection row; then the same
+    attention in passes of 8 heads, which must reproduce it bit for bit."""
     w = inputs.WORKLOADS["1m"]
     x, geom, out, lse, idx = _run(w, dev)
-    rows = inputs.sample_rows(w, 128, heads=[0, 3, 17, 28])
+    rows = inputs.sample_rows(w, 128, heads=[0, 3, 9, 14, 17, 22, 28, 31])
     st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
                                 w.scale, out, lse, idx, rows, parity.BF16_TOL)
     print("1m", st)
     st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx,
-                                   heads=[5])
-    print("1m head 5 selections", st)
+                                   heads=[5, 26])
+    print("1m heads 5, 26 selections", st)
     _check_rows_valid(w, idx, out, lse)
+    _say("1m: attention again in passes of 8 heads")
+    torch.cuda.empty_cache()
+    out2, lse2 = moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, w.topk, idx, w.scale,
+                                    head_chunk=8)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
 
 
 def test_moba_10m_sampled(dev):
@@ -306,7 +313,7 @@ def test_bucket_lists_rebuild_selection(dev):
     geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
     out, lse, idx = moba.forward(x["q"], x["k"], x["v"], geom, w.topk, w.scale)
     ws = torch.empty(moba.moba_attn_workspace_bytes(moba.MOBA_BF16, geom.total_tokens,
-                                                    geom.total_blocks, w.heads, 128, 128, 5),
+                                                    geom.total_blocks, w.heads, 128, 128, 5, 0),
                      dtype=torch.uint8, device=dev)
     moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, w.topk, idx, w.scale, workspace=ws)
     torch.cuda.synchronize()
