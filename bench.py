@@ -365,6 +365,48 @@ def measured_peaks(torch, moba, dev):
                       "of 4 GiB fp32 (bytes read + written)"}
 
 
+def measure_streamed(torch, inputs, moba, w, dev, head_chunk):
+    """One layer of a head-streamed workload (w.head_group heads at a time,
+    moba.forward_head_streamed): each group's Q/K/V are drawn on the device,
+    then the group's pool, gate and sparse attention run and its output stays
+    in device memory.  The layer time is the sum of the groups' forward times
+    (HIP events around each group's calls, the input draws excluded); the
+    wall time including the draws is reported beside it."""
+    print(f"[bench] workload {w.name}: {w.seqlens} H{w.heads} in groups of {w.head_group}, "
+          f"head_chunk {head_chunk}", file=sys.stderr, flush=True)
+    geom = moba.Geometry.make(inputs.cu_seqlens_of(w.seqlens), w.block_size, dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_groups, outs = [], {}
+
+    def source(h0, h1):
+        x = inputs.make_head_group(w, h0 // w.head_group, device=dev)
+        torch.cuda.synchronize()
+        e0.record()
+        return x["q"], x["k"], x["v"]
+
+    def on_group(h0, out, lse, idx):
+        e1.record()
+        torch.cuda.synchronize()
+        t_groups.append(e0.elapsed_time(e1))
+        outs[h0] = (out, lse)  # the layer's output stays resident, group by group
+        print(f"[bench] {w.name}: heads {h0}..{h0 + out.shape[1] - 1} {t_groups[-1]:.1f} ms",
+              file=sys.stderr, flush=True)
+
+    prof = moba.Profiler().attach()
+    prof.reset()
+    t0 = time.perf_counter()
+    moba.forward_head_streamed(source, geom, w.heads, w.head_group, w.topk, w.scale,
+                               head_chunk=head_chunk, on_group=on_group)
+    wall = (time.perf_counter() - t0) * 1e3
+    kern = prof.summary()
+    prof.detach()
+    prof.close()
+    assert all(bool(torch.isfinite(o[1]).all()) for o in outs.values())
+    del outs
+    torch.cuda.empty_cache()
+    return sum(t_groups), wall, t_groups, kern
+
+
 def measure_bwd(torch, inputs, moba, w, dev, steps, warmup):
     """Times `steps` backward passes (moba_attn_bwd: dq, dk, dv for one
     upstream gradient) of one forward's selections, after `warmup`.  Returns
@@ -419,7 +461,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="seeded query rows per worker (head), bounded by --cpu-seconds")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--also", default="8k,32k,varlen,10m,1m:bwd,1m:minmax,1m:window,1m:sink1",
+    ap.add_argument("--also", default="8k,32k,varlen,10m32,1m:bwd,1m:minmax,1m:window,1m:sink1",
                     help="comma-separated extra workloads reported under other_workloads "
                          "(ms/layer, TFLOP/s, dense, speedup); NAME:minmax uses the min/max "
                          "pooled gate, NAME:window or NAME:sinkN static routing, NAME:bwd the "
@@ -543,6 +585,33 @@ def main():
         wname, _, gate = name.partition(":")
         gate = gate or "mean"
         wo = inputs.WORKLOADS[wname]
+        if wo.head_group > 0:
+            ms_s, wall_s, per_group, kern_s = measure_streamed(torch, inputs, moba, wo, dev,
+                                                               head_chunk=wo.head_group // 2)
+            pairs_s, hist_s, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
+            n_hs, ms_hs = kern_s.get("attn_hist", (0, 0.0))
+            dense_x = (dense_ms * dense_pairs(wo.seqlens, wo.heads) / dense_pairs(w.seqlens, H)
+                       if dense_ms else None)
+            others[name] = {
+                "config": {"workload": wname, "gate": "mean", "seqlens": list(wo.seqlens),
+                           "heads": wo.heads, "head_dim": wo.head_dim,
+                           "block_size": wo.block_size, "topk": wo.topk,
+                           "head_group": wo.head_group, "head_chunk": wo.head_group // 2},
+                "steps": 1,
+                "ms_per_layer": ms_s,
+                "wall_ms_with_input_draws": wall_s,
+                "group_ms": per_group,
+                "effective_tflops": 4.0 * wo.head_dim * pairs_s / (ms_s * 1e-3) / 1e12,
+                "attn_hist_tflops": (4.0 * wo.head_dim * hist_s / (ms_hs * 1e-3) / 1e12
+                                     if ms_hs else None),
+                # the dense kernel at 10M x 32 heads would run for minutes: its time
+                # is the headline workload's measured dense rate per causal pair,
+                # scaled by the causal pairs of this layer
+                "dense_ms_extrapolated": dense_x,
+                "speedup_vs_dense_extrapolated": (dense_x / ms_s) if dense_x else None,
+                "stages_ms": {n: t for n, (c, t) in kern_s.items()},
+            }
+            continue
         if gate == "bwd":
             steps_b = min(args.also_steps, 3) if wo.total_tokens > (1 << 18) else args.also_steps
             ms_b, kern_b = measure_bwd(torch, inputs, moba, wo, dev, steps_b, max(1, args.warmup))

@@ -13,6 +13,8 @@ B = 4096, k = 12, and the 1M-token Llama setting with B = 4096, k = 12):
   32k    1 x 32768,       32 heads, d 128, B 256,  k 32, bf16, low-rank K bias
   varlen 65536/32768/16384/16384 packed, 32 heads, d 128, B 4096, k 12, bf16
   1m     1 x 1048576,     32 heads, d 128, B 4096, k 12, bf16
+  10m    1 x 10485760,    4 heads (one GPU's share of 32), d 128, B 40960, k 12, bf16
+  10m32  1 x 10485760,    32 heads in 8 streamed groups of 4, d 128, B 40960, k 12
 
 Recipe: one torch.Generator seeded with ``seed`` (default 1000 + workload
 index) on the target device draws Q, then K, then V, each i.i.d. N(0, 1) in
@@ -20,6 +22,13 @@ fp32, token-chunk by token-chunk, then rounds to the workload dtype (round to
 nearest even for bf16).  For "32k" the generator then draws, per head,
 A_h [T, 4] and C_h [4, d] i.i.d. N(0, 1) and adds 0.25 * A_h C_h (elements of
 std 0.5, rank 4) to K in fp32 before rounding.
+
+Streamed workloads (``head_group`` > 0) are too large for one GPU's memory as
+a whole layer (10M tokens x 32 heads: 86 GB per bf16 tensor), so their Q/K/V
+exist one group of heads at a time: group g (heads g * head_group ..) is drawn
+by ``make_head_group`` with the recipe above for head_group heads and the seed
+1000 + 100 * index + g, standing in for the projections that produce a head
+group's Q/K/V in a model.
 """
 
 from __future__ import annotations
@@ -41,6 +50,7 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     lowrank_bias: bool = False
     index: int = 0
+    head_group: int = 0  # > 0: the layer is streamed in groups of this many heads
 
     @property
     def total_tokens(self):
@@ -65,6 +75,9 @@ WORKLOADS = {
     # (256) kept, so B grows to 40960; 4 heads = one GPU's share of 32 heads
     # sharded by head over 8 GPUs
     "10m": Workload("10m", (10 << 20,), 4, 128, 40960, 12, "bf16", index=5),
+    # the same 10M-token layer with all 32 heads on one GPU, streamed in
+    # groups of 4 heads
+    "10m32": Workload("10m32", (10 << 20,), 32, 128, 40960, 12, "bf16", index=6, head_group=4),
 }
 
 
@@ -129,6 +142,22 @@ def make_inputs(w: Workload, device="cpu", seed=None, chunk_tokens=65536):
         _randn_into(v, gen, chunk_tokens)
     return dict(q=q, k=k, v=v, cu_seqlens=cu_seqlens_of(w.seqlens),
                 cu_blocks=cu_blocks_of(w.seqlens, w.block_size))
+
+
+def make_head_group(w: Workload, group, device="cpu", chunk_tokens=65536):
+    """Q, K, V of head group ``group`` of a streamed workload: heads
+    group * w.head_group .. (group + 1) * w.head_group - 1 as [T, head_group,
+    d] tensors (same recipe as make_inputs, seed 1000 + 100 * index + group)."""
+    if w.head_group <= 0:
+        raise ValueError(f"{w.name} is not a streamed workload")
+    h0 = group * w.head_group
+    hg = min(w.head_group, w.heads - h0)
+    if hg <= 0:
+        raise ValueError(f"{w.name} has no head group {group}")
+    wg = Workload(w.name, w.seqlens, hg, w.head_dim, w.block_size, w.topk, w.dtype,
+                  w.lowrank_bias, w.index)
+    return make_inputs(wg, device=device, seed=1000 + 100 * w.index + group,
+                       chunk_tokens=chunk_tokens)
 
 
 def sample_rows(w: Workload, per_head, seed=None, heads=None):

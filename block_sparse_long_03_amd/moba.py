@@ -366,6 +366,46 @@ def moba_attn_bwd(q, k, v, out, dout, lse, geom, topk, block_idx, scale, dq=None
     return dq, dk, dv
 
 
+def forward_head_streamed(source, geom, num_heads, group_heads, topk, scale, out_dtype=None,
+                          head_chunk=0, groups=None, on_group=None, stream=None):
+    """One MoBA layer whose heads are brought into device memory a group at a
+    time, for layers too large to hold whole ("MoBA: Learned Block Sparsity
+    for Long-Context Attention", "Efficiency and Implementation": the
+    10M-token run splits work at the level of query heads).  Heads never
+    interact in MoBA, so each group runs pool -> gate -> sparse attention on
+    its own, in one workspace (sized for group_heads heads in passes of
+    head_chunk) reused by every group.
+
+    source(h0, h1) returns device tensors (q, k, v) [T, h1 - h0, d] for heads
+    h0 .. h1 - 1 (a host-to-device copy, a projection, a generator).
+    groups: indices of the groups to run (default all).  on_group(h0, out,
+    lse, block_idx) receives each group's results; without it the (h0, out,
+    lse) of every group are returned."""
+    ngroups = (num_heads + group_heads - 1) // group_heads
+    ws = None
+    results = []
+    for g in (range(ngroups) if groups is None else groups):
+        h0 = g * group_heads
+        h1 = min(num_heads, h0 + group_heads)
+        q, k, v = source(h0, h1)
+        H, d = _qkv_shape(q, geom)
+        if H != h1 - h0:
+            raise ValueError("source returned the wrong number of heads")
+        if ws is None:
+            ws = _workspace(moba_attn_workspace_bytes(
+                _dtype_code(q.dtype), geom.total_tokens, geom.total_blocks, group_heads, d,
+                geom.block_size, topk, head_chunk), q.device)
+        out, lse, idx = forward(q, k, v, geom, topk, scale, out_dtype=out_dtype, workspace=ws,
+                                stream=stream, head_chunk=head_chunk)
+        del q, k, v
+        if on_group is not None:
+            on_group(h0, out, lse, idx)
+        else:
+            results.append((h0, out, lse))
+        del idx
+    return results
+
+
 def forward_minmax(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=None):
     """MoBA with the min/max pooled gate: pool_minmax -> gate -> sparse
     attention.  Returns (out, lse, block_idx)."""

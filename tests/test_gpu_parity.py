@@ -161,18 +161,39 @@ def test_moba_1m_sampled(dev):
     assert torch.equal(out2, out) and torch.equal(lse2, lse)
 
 
-def test_moba_10m_sampled(dev):
+def test_moba_10m_streamed(dev):
     """Constant sparsity at 10M tokens (B 40960 keeps the 1M workload's 256
-    blocks), one GPU's 4-head share: outputs and selections on 64 seeded
-    rows of two heads, causal validity of every selection row."""
-    w = inputs.WORKLOADS["10m"]
-    x, geom, out, lse, idx = _run(w, dev)
-    rows = inputs.sample_rows(w, 32, heads=[0, 3])
-    st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
-                                w.scale, out, lse, idx, rows, parity.BF16_TOL)
-    print("10m", st)
-    _check_rows_valid(w, idx, out, lse)
-    del x, out, lse, idx
+    blocks) with all 32 heads on one GPU, streamed group by group
+    (forward_head_streamed, groups of 4 heads in passes of 2): the first
+    and the last of the 8 head groups run; outputs and selections on 48
+    seeded rows of four heads in them, causal validity of every selection
+    row of both groups."""
+    w = inputs.WORKLOADS["10m32"]
+    _say(w.name, "groups 0 and 7 of", w.heads // w.head_group, "B", w.block_size, "k", w.topk)
+    geom = moba.Geometry.make(inputs.cu_seqlens_of(w.seqlens), w.block_size, dev)
+    check_heads = {0: [1, 3], 7: [28, 31]}
+
+    def source(h0, h1):
+        _say(w.name, "heads", h0, "..", h1 - 1)
+        x = inputs.make_head_group(w, h0 // w.head_group, device=dev)
+        return x["q"], x["k"], x["v"]
+
+    def on_group(h0, out, lse, idx):
+        torch.cuda.synchronize()
+        g = h0 // w.head_group
+        wg = inputs.custom(w.seqlens, out.shape[1], w.head_dim, w.block_size, w.topk, w.dtype)
+        _check_rows_valid(wg, idx, out, lse)
+        x = inputs.make_head_group(w, g, device=dev)  # the same draw again
+        hs = [h - h0 for h in check_heads[g]]
+        rows = inputs.sample_rows(w, 24, heads=hs)
+        st = parity.check_moba_rows(x["q"], x["k"], x["v"], inputs.cu_seqlens_of(w.seqlens),
+                                    w.block_size, w.topk, w.scale, out, lse, idx, rows,
+                                    parity.BF16_TOL)
+        print("10m32 group", g, st)
+        del x
+
+    moba.forward_head_streamed(source, geom, w.heads, w.head_group, w.topk, w.scale,
+                               head_chunk=2, groups=[0, 7], on_group=on_group)
     torch.cuda.empty_cache()
 
 
