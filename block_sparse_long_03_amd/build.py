@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoba.so")
 SOURCES = ["api.cpp", "pool_gate.hip", "bucket_merge.hip", "attn_mfma.hip", "attn_f32.hip",
-           "attn_bwd.hip", "probe.hip"]
+           "attn_bwd.hip", "probe.hip", "static_ws.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

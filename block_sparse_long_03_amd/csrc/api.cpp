@@ -448,6 +448,44 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
   return MOBA_OK;
 }
 
+moba_status moba_attn_fwd_static(const void* q, const void* k, const void* v, int dtype,
+                                 const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                 int num_seqs, int total_tokens, int max_seqlen,
+                                 int total_blocks, int num_heads, int head_dim,
+                                 int block_size, int topk, const int32_t* block_idx,
+                                 float softmax_scale, void* out, int out_dtype, float* lse,
+                                 void* stream) {
+  // everything that can be checked without the device first: an invalid or
+  // oversized call touches nothing
+  moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                                  max_seqlen, total_blocks, num_heads, head_dim, block_size);
+  if (st != MOBA_OK) return st;
+  st = check_topk(total_tokens, topk);
+  if (st != MOBA_OK) return st;
+  if (!dtype_ok(out_dtype)) return MOBA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MOBA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MOBA_OK;
+  if (!q || !k || !v || !block_idx || !out || !lse) return MOBA_ERR_INVALID_ARG;
+  // the most heads per pass whose workspace fits the fixed array
+  const bool bf16 = dtype == MOBA_BF16;
+  auto need = [&](int hc) {
+    return moba::attn_workspace_layout(bf16, total_tokens, total_blocks, hc, head_dim,
+                                       block_size, topk)
+        .total;
+  };
+  const size_t one = need(1);
+  if (one > (size_t)MOBA_STATIC_WORKSPACE_BYTES) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+  int hc = (int)std::min<size_t>((size_t)num_heads, (size_t)MOBA_STATIC_WORKSPACE_BYTES / one);
+  while (hc > 1 && need(hc) > (size_t)MOBA_STATIC_WORKSPACE_BYTES) --hc;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipError_t e = moba::static_workspace(&ws, &ws_bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  return moba_attn_fwd(q, k, v, dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
+                       max_seqlen, total_blocks, num_heads, head_dim, block_size, topk,
+                       block_idx, softmax_scale, out, out_dtype, lse, hc, ws, ws_bytes, stream);
+}
+
 size_t moba_attn_bwd_workspace_bytes(int dtype, int total_tokens, int total_blocks,
                                      int num_heads, int head_dim, int block_size, int topk) {
   if (dtype != MOBA_BF16 || total_tokens < 0 || total_blocks < 0 || num_heads < 1 ||

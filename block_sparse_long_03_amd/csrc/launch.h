@@ -137,6 +137,10 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int topk, float scale, const int32_t* list, const int4* tile_info,
                         long long hist_tiles, float* dq, hipStream_t st);
 
+// The device address of the library's fixed workspace on the current device
+// (MOBA_STATIC_WORKSPACE_BYTES, looked up once per device) and its size.
+hipError_t static_workspace(void** ptr, size_t* bytes);
+
 // Measurement support: `workgroups` x 4 waves, each running 4 independent
 // chains of `iterations` 32x32x16 bf16 MFMAs (2 * 32 * 32 * 16 flops each);
 // operands 0 = fixed register operands, 1 = random register operands,

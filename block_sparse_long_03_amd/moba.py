@@ -27,11 +27,11 @@ MOBA_ERR_HIP = -4
 MOBA_F32 = 0
 MOBA_BF16 = 1
 # the MOBA_API_VERSION of include/moba.h these bindings are written for
-API_VERSION = 3
+API_VERSION = 4
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
-           "moba_attn_workspace_bytes", "moba_attn_fwd",
+           "moba_attn_workspace_bytes", "moba_attn_fwd", "moba_attn_fwd_static",
            "moba_attn_bwd_workspace_bytes", "moba_attn_bwd",
            "moba_dense_workspace_bytes", "moba_dense_causal_fwd", "moba_profiler_create",
            "moba_profiler_attach", "moba_profiler_reset", "moba_profiler_read",
@@ -81,6 +81,8 @@ def lib():
     L.moba_attn_fwd.restype = i32
     L.moba_attn_fwd.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, i32, vp, sz,
                                                           vp]
+    L.moba_attn_fwd_static.restype = i32
+    L.moba_attn_fwd_static.argtypes = [vp, vp, vp, i32] + geo + [i32, vp, f32, vp, i32, vp, vp]
     L.moba_attn_bwd_workspace_bytes.restype = sz
     L.moba_attn_bwd_workspace_bytes.argtypes = [i32] * 7
     L.moba_attn_bwd.restype = i32
@@ -274,6 +276,17 @@ def moba_attn_fwd(q, k, v, geom, topk, block_idx, scale, out=None, out_dtype=Non
         _ptr(q), _ptr(k), _ptr(v), dt, *geom.args(H, d), int(topk), _ptr(block_idx),
         float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), int(head_chunk),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def moba_attn_fwd_static(q, k, v, geom, topk, block_idx, scale, out, lse, stream=None):
+    """moba_attn_fwd with the library's fixed device workspace: the call
+    allocates nothing (out and lse are the caller's tensors)."""
+    H, d = _qkv_shape(q, geom)
+    _check("moba_attn_fwd_static", lib().moba_attn_fwd_static(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), *geom.args(H, d), int(topk),
+        _ptr(block_idx), float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse),
+        _stream(stream)))
     return out, lse
 
 

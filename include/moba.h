@@ -57,7 +57,11 @@
 extern "C" {
 #endif
 
-#define MOBA_API_VERSION 3
+#define MOBA_API_VERSION 4
+
+/* Size of the device workspace moba_attn_fwd_static keeps inside the library
+ * (per GPU, for the life of the process). */
+#define MOBA_STATIC_WORKSPACE_BYTES (256u << 20)
 
 typedef enum moba_status {
   MOBA_OK = 0,
@@ -232,6 +236,34 @@ moba_status moba_attn_fwd(const void* q, const void* k, const void* v, int dtype
                           float softmax_scale, void* out, int out_dtype,
                           float* lse, int head_chunk, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * moba_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, with the workspace taken from a fixed
+ * device array inside the library instead of a caller buffer.  The array
+ * holds MOBA_STATIC_WORKSPACE_BYTES (256 MiB) on each GPU the library runs
+ * on, from the first call on that GPU until the process ends; the call
+ * itself allocates nothing.
+ *   Arguments as for moba_attn_fwd, without head_chunk and the workspace.
+ *   The heads run in passes of as many heads as fit in the array
+ *   (moba_attn_workspace_bytes(..., head_chunk) <= MOBA_STATIC_WORKSPACE_BYTES);
+ *   when not even one head fits (about total_tokens * topk * (2 head_dim + 8)
+ *   bytes per head, e.g. 32K tokens at topk 32 and head_dim 128), the call
+ *   returns MOBA_ERR_WORKSPACE_TOO_SMALL and launches nothing.
+ *   Every call on one GPU uses that GPU's one array, and the array keeps the
+ *   last call's contents (every piece a call reads is written or cleared by
+ *   that call first).  Calls that overlap on one GPU (on different streams,
+ *   or from several threads without ordering) race on the array and give
+ *   wrong results: serialise them.
+ */
+moba_status moba_attn_fwd_static(const void* q, const void* k, const void* v, int dtype,
+                                 const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                 int num_seqs, int total_tokens, int max_seqlen,
+                                 int total_blocks, int num_heads, int head_dim,
+                                 int block_size, int topk, const int32_t* block_idx,
+                                 float softmax_scale, void* out, int out_dtype, float* lse,
+                                 void* stream);
 
 /*
  * Backward of moba_attn_fwd: gradients of out with respect to q, k and v for

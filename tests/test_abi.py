@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(moba.EXPORTS)
@@ -180,6 +180,28 @@ def test_head_chunk_workspace(L):
     assert L.moba_attn_workspace_bytes(1, 1000, 8, 4, 128, 128, 3, -1) == 0
     # a workspace sized for passes of one head is too small for all heads at once
     assert attn(L, ws_bytes=one, H=4) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
+
+
+def static_fwd(L, topk=3, scale=0.1, **kw):
+    g = dict(GEO, **kw)
+    return L.moba_attn_fwd_static(FAKE, FAKE, FAKE, kw.get("dtype", 1), g["cu"], g["cb"], g["S"],
+                                  g["T"], g["maxL"], g["NB"], g["H"], g["d"], g["B"], topk,
+                                  kw.get("idx", FAKE), ctypes.c_float(scale), FAKE, 1, FAKE,
+                                  None)
+
+
+def test_static_workspace_limits(L):
+    """moba_attn_fwd_static rejects, before touching the device, geometries
+    whose single head needs more than the library's fixed workspace."""
+    assert "#define MOBA_STATIC_WORKSPACE_BYTES (256u << 20)" in open(HEADER).read()
+    limit = 256 << 20
+    big = dict(T=32768, maxL=32768, NB=128, H=1, d=128, B=256)
+    assert L.moba_attn_workspace_bytes(1, 32768, 128, 1, 128, 256, 32, 1) > limit
+    assert static_fwd(L, topk=32, **big) == moba.MOBA_ERR_WORKSPACE_TOO_SMALL
+    assert static_fwd(L, topk=0) == moba.MOBA_ERR_INVALID_ARG
+    assert static_fwd(L, idx=None) == moba.MOBA_ERR_INVALID_ARG
+    assert static_fwd(L, scale=-1.0) == moba.MOBA_ERR_INVALID_ARG
+    assert static_fwd(L, T=0, maxL=0, NB=0) == moba.MOBA_OK
 
 
 def test_workspace_too_small(L):
