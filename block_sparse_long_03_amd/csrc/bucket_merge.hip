@@ -13,26 +13,20 @@
 
 namespace moba {
 
-constexpr int kBucketTokensMax = 256;  // tokens per workgroup in count/scatter (all heads)
+constexpr int kBucketTokensMax = 256;  // tokens per workgroup of the count pass (all heads)
 constexpr int kBucketLdsBins = 8192;  // LDS histogram limit (heads x past blocks per tile)
 
-// Per (sequence tile of `tile_tokens` tokens): every (token, head) row of
-// block_idx for the HC heads h0 .. h0 + HC - 1 of the group, read in memory
-// order (consecutive lanes take consecutive rows, so a wave reads one
-// contiguous range per token), counted into an LDS histogram per (head of the
-// group, past block) and flushed with one global atomic per touched bin.
-// The scatter pass reserves a range per bin, then places each entry: the
-// global token times slot_stride plus its slot, or (slot_stride 0) the token
-// alone.
-template <bool kScatter>
-__global__ __launch_bounds__(256) void bucket_pass_kernel(
+// Count pass, per (sequence tile of `tile_tokens` tokens): every (token,
+// head) row of block_idx for the HC heads h0 .. h0 + HC - 1 of the group,
+// read in memory order (consecutive lanes take consecutive rows, so a wave
+// reads one contiguous range per token), counted into an LDS histogram per
+// (head of the group, past block) and flushed with one global atomic per
+// touched bin.
+__global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int tile_tokens,
-    int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
-    int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ list) {
+    int H, int h0, int HC, int NB, int block_size, int topk, int32_t* __restrict__ counts) {
   __shared__ int32_t hist[kBucketLdsBins];
-  __shared__ int32_t basev[kScatter ? kBucketLdsBins : 1];
   const int sid = blockIdx.x / tiles_per_seq;
   const int tile = blockIdx.x % tiles_per_seq;
   int start, len;
@@ -50,8 +44,8 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
     __syncthreads();
   }
   // walks row r = (p - p0) * HC + h of the group (head h0 + h), calling
-  // f(h, e, slot, p) for each accepted historical entry (0 <= e < c,
-  // increasing, inside the batch's blocks)
+  // f(h, e) for each accepted historical entry (0 <= e < c, increasing,
+  // inside the batch's blocks)
   auto walk = [&](int r, auto&& f) {
     const int p = p0 + r / HC;
     const int h = r - (r / HC) * HC;
@@ -59,9 +53,9 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
     const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * topk;
     int last = -1, nh = 0;
     auto visit = [&](int e) {
-      if (e >= 0 && e < c && e > last) {
+      if (accept_hist(e, c, last, nh, topk)) {
         last = e;
-        if (gb0 + e < NB) f(h, e, nh, p);  // else inconsistent geometry: dropped
+        if (gb0 + e < NB) f(h, e);  // else inconsistent geometry: dropped
         ++nh;
       }
     };
@@ -77,45 +71,149 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(
       for (int j = 0; j < topk; ++j) visit(row[j]);
     }
   };
-  if (!kScatter) {
-    for (int r = threadIdx.x; r < nrows; r += 256)
-      walk(r, [&](int h, int e, int, int) {
-        if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
-        else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
-      });
-    if (!use_lds) return;
-    __syncthreads();
-    for (int b = threadIdx.x; b < nbins * HC; b += 256) {
-      const int h = b / nbins, e = b - (b / nbins) * nbins;
-      if (hist[b]) atomicAdd(&counts[(size_t)h * NB + gb0 + e], hist[b]);
-    }
-    return;
-  }
-  if (!use_lds) {
-    for (int r = threadIdx.x; r < nrows; r += 256)
-      walk(r, [&](int h, int e, int slot, int p) {
-        const size_t key = (size_t)h * NB + gb0 + e;
-        list[offsets[key] + atomicAdd(&counts[key], 1)] = slot_stride ? (start + p) * slot_stride + slot : start + p;
-      });
-    return;
-  }
   for (int r = threadIdx.x; r < nrows; r += 256)
-    walk(r, [&](int h, int e, int, int) { atomicAdd(&hist[h * nbins + e], 1); });
+    walk(r, [&](int h, int e) {
+      if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
+      else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
+    });
+  if (!use_lds) return;
   __syncthreads();
-  // reserve a range per touched bin, then place every entry
   for (int b = threadIdx.x; b < nbins * HC; b += 256) {
     const int h = b / nbins, e = b - (b / nbins) * nbins;
+    if (hist[b]) atomicAdd(&counts[(size_t)h * NB + gb0 + e], hist[b]);
+  }
+}
+
+// Scatter of one head's entries of a token tile into the per-(head, block)
+// lists, staged in LDS so that every block's run is written by consecutive
+// lanes.  The tile's entries are counted per past block into an LDS
+// histogram, each non-empty block reserves its range of the list with one
+// global atomic, the entries are placed into an LDS staging array grouped by
+// block (positions from LDS atomics), and each wave then copies whole runs
+// out.  A run of a block holds every entry of the tile's R tokens that
+// selected it (about R (k - 1) / n of them), so the list is written in long
+// contiguous runs instead of one scattered word per entry.  Tiles whose
+// tokens have more past blocks than the LDS histogram holds place their
+// entries with global atomics instead.  Workgroups run over (token tile,
+// head of the group) with the heads of one tile on one XCD, where they share
+// the L2 lines of the tile's block_idx rows.
+constexpr int kScatterBins = 1024;
+constexpr int kScatterStage = 12288;  // staged entries per workgroup
+
+// tokens per scatter tile for rows of k - 1 historical slots: the largest
+// power of two in [32, 1024] whose entries fit the staging array
+inline int scatter_tile_tokens(int topk) {
+  int r = 1024;
+  while (r > 32 && (long long)r * (topk - 1) > kScatterStage) r >>= 1;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void bucket_scatter_kernel(
+    const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int nunits,
+    int tile_tokens, int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
+    int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ list) {
+  __shared__ int32_t hist[kScatterBins];
+  __shared__ int32_t loff[kScatterBins + 1];
+  __shared__ int32_t gbase[kScatterBins];
+  __shared__ int32_t stage[kScatterStage];
+  // XCD-contiguous order: workgroup b runs on XCD b % 8; XCD x takes units
+  // x, x + 8, ... and, for each, the HC heads one after the other
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int unit = x + kXcds * (j / HC);
+  const int hl = j % HC;
+  if (unit >= nunits) return;
+  const int sid = unit / tiles_per_seq;
+  const int tile = unit % tiles_per_seq;
+  int start, len;
+  seq_span(cu_seqlens, sid, total_tokens, &start, &len);
+  const int p0 = tile * tile_tokens;
+  if (p0 >= len) return;
+  const int p1 = min(len, p0 + tile_tokens);
+  const int nbins = (p1 - 1) / block_size;  // past blocks of the last row
+  if (nbins == 0) return;
+  const int gb0 = cu_blocks[sid];
+  const size_t key0 = (size_t)hl * NB + gb0;
+  // calls f(e, slot, p) for each accepted historical entry of row p (the
+  // rule of accept_hist, inside the batch's blocks): at most topk - 1 per
+  // row, so a tile stages at most tile_tokens * (topk - 1) entries
+  auto walk = [&](int p, auto&& f) {
+    const int c = p / block_size;
+    const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + hl) * topk;
+    int last = -1, nh = 0;
+    auto visit = [&](int e) {
+      if (accept_hist(e, c, last, nh, topk)) {
+        last = e;
+        if (gb0 + e < NB) f(e, nh, p);  // else inconsistent geometry: dropped
+        ++nh;
+      }
+    };
+    if ((topk & 3) == 0) {
+      for (int q = 0; q < topk; q += 4) {
+        const int4 e4 = *reinterpret_cast<const int4*>(row + q);
+        visit(e4.x);
+        visit(e4.y);
+        visit(e4.z);
+        visit(e4.w);
+      }
+    } else {
+      for (int q = 0; q < topk; ++q) visit(row[q]);
+    }
+  };
+  auto value = [&](int slot, int p) {
+    return slot_stride ? (start + p) * slot_stride + slot : start + p;
+  };
+  if (nbins > kScatterBins) {
+    for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+      walk(p, [&](int e, int slot, int pp) {
+        const size_t key = key0 + e;
+        list[offsets[key] + atomicAdd(&counts[key], 1)] = value(slot, pp);
+      });
+    return;
+  }
+  for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0;
+  __syncthreads();
+  for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+    walk(p, [&](int e, int, int) { atomicAdd(&hist[e], 1); });
+  __syncthreads();
+  // exclusive scan of the histogram (one wave), global range per block
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int b0 = 0; b0 < nbins; b0 += 64) {
+      const int b = b0 + lane;
+      const int v = b < nbins ? hist[b] : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(inc, d);
+        if (lane >= d) inc += u;
+      }
+      if (b < nbins) loff[b] = carry + inc - v;
+      carry += __shfl(inc, 63);
+    }
+    if (lane == 0) loff[nbins] = carry;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nbins; b += 256) {
     const int n = hist[b];
-    const size_t key = (size_t)h * NB + gb0 + e;
-    basev[b] = n ? offsets[key] + atomicAdd(&counts[key], n) : 0;
+    gbase[b] = n ? offsets[key0 + b] + atomicAdd(&counts[key0 + b], n) : 0;
     hist[b] = 0;
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < nrows; r += 256)
-    walk(r, [&](int h, int e, int slot, int p) {
-      const int b = h * nbins + e;
-      list[basev[b] + atomicAdd(&hist[b], 1)] = slot_stride ? (start + p) * slot_stride + slot : start + p;
+  for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+    walk(p, [&](int e, int slot, int pp) {
+      stage[loff[e] + atomicAdd(&hist[e], 1)] = value(slot, pp);
     });
+  __syncthreads();
+  // each wave copies whole runs: lanes write consecutive list entries
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int b = wv; b < nbins; b += 4) {
+    const int a = loff[b], n = loff[b + 1] - a;
+    int32_t* dst = list + gbase[b];
+    for (int i = lane; i < n; i += 64) dst[i] = stage[a + i];
+  }
 }
 
 // Exclusive scans of the per-(head, block) counts (entries and tiles of
@@ -193,17 +291,21 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
   const int tiles = (g.max_seqlen + tile_tokens - 1) / tile_tokens;
   dim3 grid(g.num_seqs * tiles);
   if (tiles > 0 && topk > 1)
-    hipLaunchKernelGGL((bucket_pass_kernel<false>), grid, dim3(256), 0, st, block_idx,
-                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk, slot_stride,
-                       counts, offsets, list);
+    hipLaunchKernelGGL(bucket_count_kernel, grid, dim3(256), 0, st, block_idx, g.cu_seqlens,
+                       g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads, g.head_lo,
+                       g.head_cnt, g.total_blocks, g.block_size, topk, counts);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, st, counts, n, tile_q,
                      offsets, tile_offsets);
-  if (tiles > 0 && topk > 1)
-    hipLaunchKernelGGL((bucket_pass_kernel<true>), grid, dim3(256), 0, st, block_idx,
-                       g.cu_seqlens, g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads,
-                       g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk, slot_stride,
-                       counts, offsets, list);
+  if (tiles > 0 && topk > 1) {
+    const int rt = scatter_tile_tokens(topk);
+    const int stiles = (g.max_seqlen + rt - 1) / rt;
+    const int nunits = g.num_seqs * stiles;
+    const long long wgs = (long long)((nunits + kXcds - 1) / kXcds) * kXcds * g.head_cnt;
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)wgs), dim3(256), 0, st, block_idx,
+                       g.cu_seqlens, g.cu_blocks, g.total_tokens, stiles, nunits, rt,
+                       g.num_heads, g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk,
+                       slot_stride, counts, offsets, list);
+  }
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
                        st, offsets, tile_offsets, n, tile_q, max_tiles, tile_info);

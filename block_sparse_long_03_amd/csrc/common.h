@@ -117,15 +117,18 @@ __device__ __forceinline__ void seq_span(const int32_t* __restrict__ cu_seqlens,
 }
 
 // Walks a block_idx row and reports, for each entry, whether it is a
-// historical selection (0 <= e < c and larger than the previous accepted
-// entry).  Accepted historical entries get consecutive slots 0, 1, ...; the
-// own block always uses slot topk - 1.  Both the bucketing and the merge
-// apply exactly this rule.
+// historical selection (0 <= e < c, larger than the previous accepted entry,
+// and among the first topk - 1 such entries).  Accepted historical entries
+// get consecutive slots 0 .. topk - 2; the own block always uses slot
+// topk - 1.  The bucketing passes and the merge apply exactly this rule.
+__device__ __forceinline__ bool accept_hist(int e, int c, int last, int nh, int topk) {
+  return e >= 0 && e < c && e > last && nh < topk - 1;
+}
 __device__ __forceinline__ int count_hist(const int32_t* __restrict__ row, int topk, int c) {
   int nh = 0, last = -1;
   for (int j = 0; j < topk; ++j) {
     int e = row[j];
-    if (e >= 0 && e < c && e > last) { ++nh; last = e; }
+    if (accept_hist(e, c, last, nh, topk)) { ++nh; last = e; }
   }
   return nh;
 }

@@ -209,7 +209,8 @@ size_t moba_attn_workspace_bytes(int dtype, int total_tokens, int total_blocks,
  *   block_idx  as written by moba_gate_topk (or any caller-made selection in
  *              the same format: ascending, then -1).  Entries that are
  *              negative, not below the own block, or not increasing are
- *              ignored; the own block is always attended.
+ *              ignored, as is any historical entry after the first
+ *              topk - 1; the own block is always attended.
  *   out        [total_tokens, num_heads, head_dim], out_dtype (F32 or BF16)
  *   lse        [total_tokens, num_heads] fp32, natural log
  *   head_chunk heads per pass (0 or >= num_heads: all heads at once).  The
