@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
 // head of the group) with the heads of one tile on one XCD, where they share
 // the L2 lines of the tile's block_idx rows.
 constexpr int kScatterBins = 1024;
+constexpr int kScatterThreads = 1024;  // one token row per thread: the row loads of a walk fly together
 constexpr int kScatterStage = 12288;  // staged entries per workgroup
 
 // tokens per scatter tile for rows of k - 1 historical slots: the largest
@@ -108,7 +109,7 @@ inline int scatter_tile_tokens(int topk) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void bucket_scatter_kernel(
+__global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int nunits,
     int tile_tokens, int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
@@ -165,16 +166,16 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     return slot_stride ? (start + p) * slot_stride + slot : start + p;
   };
   if (nbins > kScatterBins) {
-    for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+    for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
       walk(p, [&](int e, int slot, int pp) {
         const size_t key = key0 + e;
         list[offsets[key] + atomicAdd(&counts[key], 1)] = value(slot, pp);
       });
     return;
   }
-  for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0;
+  for (int b = threadIdx.x; b < nbins; b += kScatterThreads) hist[b] = 0;
   __syncthreads();
-  for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+  for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
     walk(p, [&](int e, int, int) { atomicAdd(&hist[e], 1); });
   __syncthreads();
   // exclusive scan of the histogram (one wave), global range per block
@@ -196,20 +197,20 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     if (lane == 0) loff[nbins] = carry;
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nbins; b += 256) {
+  for (int b = threadIdx.x; b < nbins; b += kScatterThreads) {
     const int n = hist[b];
     gbase[b] = n ? offsets[key0 + b] + atomicAdd(&counts[key0 + b], n) : 0;
     hist[b] = 0;
   }
   __syncthreads();
-  for (int p = p0 + (int)threadIdx.x; p < p1; p += 256)
+  for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
     walk(p, [&](int e, int slot, int pp) {
       stage[loff[e] + atomicAdd(&hist[e], 1)] = value(slot, pp);
     });
   __syncthreads();
   // each wave copies whole runs: lanes write consecutive list entries
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int b = wv; b < nbins; b += 4) {
+  for (int b = wv; b < nbins; b += kScatterThreads / 64) {
     const int a = loff[b], n = loff[b + 1] - a;
     int32_t* dst = list + gbase[b];
     for (int i = lane; i < n; i += 64) dst[i] = stage[a + i];
@@ -301,7 +302,8 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
     const int stiles = (g.max_seqlen + rt - 1) / rt;
     const int nunits = g.num_seqs * stiles;
     const long long wgs = (long long)((nunits + kXcds - 1) / kXcds) * kXcds * g.head_cnt;
-    hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)wgs), dim3(256), 0, st, block_idx,
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)wgs), dim3(kScatterThreads), 0, st,
+                       block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, stiles, nunits, rt,
                        g.num_heads, g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk,
                        slot_stride, counts, offsets, list);
