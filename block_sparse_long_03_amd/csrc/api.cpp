@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -156,6 +157,8 @@ struct BwdWorkspace {
 };
 
 constexpr int kBwdTileQ = 128;
+// one workgroup per CU
+constexpr long long kPrefixMinGrid = 256;
 
 long long bwd_tiles_bound(long long T, long long NB, long long H, long long topk) {
   if (topk < 2) return 0;
@@ -201,6 +204,7 @@ AttnWorkspace attn_workspace_layout(bool bf16, long long T, long long NB, long l
   w.vt = take(bf16 ? (size_t)(NB * B * H * D) * 2 : 0);
   w.tile_info = take(bf16 ? (size_t)hist_tiles_bound(T, NB, H, D, B, topk) * 16 : 0);
   w.vmax = take((size_t)H * 4);
+  w.notfull = take(bf16 ? nkeys * 4 : 0);
   w.total = off;
   return w;
 }
@@ -216,7 +220,13 @@ namespace {
 
 // One pass of moba_attn_fwd over the heads of g's group: V staging, bucketing,
 // historical and own-block attention into the group's partials, merge into
-// out and lse.
+// out and lse.  bf16: rows of a sequence's first topk blocks that select every
+// earlier block (all of them under the gate) attend to their whole causal
+// prefix, so the dense kernel writes them directly (stage "attn_prefix") and
+// bucketing, the own-block pass and the merge skip them.  This route is taken
+// when the prefix launch fills the chip (kPrefixMinGrid workgroups): a
+// smaller one runs for as long as its heaviest tile (topk * block_size keys)
+// takes, longer than the passes it saves.
 moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, const moba::Geo& g,
                       int topk, const int32_t* block_idx, float softmax_scale, void* out,
                       int out_dtype, float* lse, char* ws, const moba::AttnWorkspace& L,
@@ -231,17 +241,28 @@ moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, co
   uint32_t* vmax = (uint32_t*)(ws + L.vmax);
   const bool out_bf16 = out_dtype == MOBA_BF16;
   hipError_t e;
+  int dense_blocks = 0;  // rows of blocks below it may take the dense-prefix route
 
   if (bf16) {
     uint16_t* vt = (uint16_t*)(ws + L.vt);
     int4* tile_info = (int4*)(ws + L.tile_info);
+    int32_t* notfull = (int32_t*)(ws + L.notfull);
+    const int q_limit = (int)std::min<long long>((long long)topk * g.block_size, INT_MAX);
+    if (moba::dense_grid(g, q_limit) >= moba::kPrefixMinGrid) dense_blocks = topk;
     if ((e = timed("v_stage", s, [&] { return moba::launch_v_transpose(v, g, vmax, vt, s); })) !=
         hipSuccess)
       return hip_fail(e);
     if ((e = timed("bucket", s, [&] {
            return moba::launch_bucket(block_idx, g, topk,
                                       moba::hist_tile_q(g.block_size, g.head_dim), counts,
-                                      offsets, tile_offsets, list, tile_info, tiles, s);
+                                      offsets, tile_offsets, list, tile_info, tiles, s, false,
+                                      dense_blocks, notfull);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if (dense_blocks > 0 &&
+        (e = timed("attn_prefix", s, [&] {
+           return moba::launch_attn_mfma_dense(q, k, vt, vmax, g, softmax_scale, out, out_bf16,
+                                               lse, s, q_limit);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = timed("attn_hist", s, [&] {
@@ -251,7 +272,8 @@ moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, co
       return hip_fail(e);
     if ((e = timed("attn_own", s, [&] {
            return moba::launch_attn_mfma_own(q, k, vt, g, topk, softmax_scale,
-                                             (uint16_t*)o_part, lse_part, s);
+                                             (uint16_t*)o_part, lse_part, dense_blocks,
+                                             notfull, s);
          })) != hipSuccess)
       return hip_fail(e);
   } else {
@@ -274,8 +296,8 @@ moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, co
       return hip_fail(e);
   }
   if ((e = timed("merge", s, [&] {
-         return moba::launch_merge(block_idx, g, topk, o_part, bf16, lse_part, vmax, out,
-                                   out_bf16, lse, s);
+         return moba::launch_merge(block_idx, g, topk, dense_blocks, o_part, bf16, lse_part,
+                                   vmax, out, out_bf16, lse, s);
        })) != hipSuccess)
     return hip_fail(e);
   return MOBA_OK;

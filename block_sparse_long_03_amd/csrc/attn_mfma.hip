@@ -67,6 +67,9 @@ struct MfmaArgs {
   int num_seqs, total_tokens, H, Hs, h0, block_size, topk, NB;
   int tiles_per_unit;  // own: query tiles per block; dense: query tiles per sequence
   int units_per_seq;   // own: max blocks per sequence
+  int q_limit;         // dense: queries at local positions below it only
+  int dense_blocks;    // own: blocks below it whose notfull flag is 0 are skipped
+  const int32_t* notfull;
   float scale2;        // softmax scale * log2(e)
   const int32_t* list;
   const int4* tile_info;  // hist: {key, first entry, end entry, 0} per tile, key < 0 past the end
@@ -156,13 +159,18 @@ void attn_mfma_kernel(MfmaArgs a) {
     if (MODE == kModeOwn) {
       const int c = rem / a.tiles_per_unit;
       const int sub = rem % a.tiles_per_unit;
+      // every row of a block below dense_blocks with notfull 0 is written by
+      // the dense-prefix pass
+      if (c < a.dense_blocks && gb_base + c < a.NB &&
+          a.notfull[(size_t)h * a.NB + gb_base + c] == 0)
+        return;
       const int blo = c * a.block_size;
       q_lo = blo + sub * TQ;
       q_hi = min(min(q_lo + TQ, blo + a.block_size), seq_len);
       key_lo = blo;
     } else {
       q_lo = rem * TQ;
-      q_hi = min(q_lo + TQ, seq_len);
+      q_hi = min(min(q_lo + TQ, seq_len), a.q_limit);
       key_lo = 0;
     }
     if (q_lo >= q_hi) return;
@@ -580,6 +588,7 @@ static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, cons
   a.topk = topk;
   a.NB = g.total_blocks;
   a.scale2 = scale * kLog2e;
+  a.q_limit = 0x7fffffff;
   return a;
 }
 
@@ -620,9 +629,12 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
 
 hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt,
                                 const Geo& g, int topk, float scale, uint16_t* o_part,
-                                float* lse_part, hipStream_t st) {
+                                float* lse_part, int dense_blocks, const int32_t* notfull,
+                                hipStream_t st) {
   if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, topk, scale);
+  a.dense_blocks = dense_blocks;
+  a.notfull = notfull;
   // own-block tiles span at most one block of keys: 4 waves
   const int waves = 4;
   a.tiles_per_unit = (g.block_size + 32 * waves - 1) / (32 * waves);
@@ -637,12 +649,15 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
 
 hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
                                   const uint32_t* vmax_bits, const Geo& g, float scale,
-                                  void* out, bool out_bf16, float* lse, hipStream_t st) {
-  if (g.total_tokens == 0 || g.max_seqlen == 0) return hipSuccess;
+                                  void* out, bool out_bf16, float* lse, hipStream_t st,
+                                  int q_limit) {
+  if (g.total_tokens == 0 || g.max_seqlen == 0 || q_limit <= 0) return hipSuccess;
   MfmaArgs a = base_args(q, k, vt, g, 1, scale);
   a.vmax_bits = vmax_bits;
-  const int waves = mfma_waves(g.max_seqlen);
-  a.tiles_per_unit = (g.max_seqlen + 32 * waves - 1) / (32 * waves);
+  a.q_limit = q_limit;
+  const int span = min(g.max_seqlen, q_limit);  // query positions of the longest sequence
+  const int waves = mfma_waves(span);
+  a.tiles_per_unit = (span + 32 * waves - 1) / (32 * waves);  // dense_grid's tiles
   a.units_per_seq = 1;
   a.o_out = out;
   a.lse_out = lse;

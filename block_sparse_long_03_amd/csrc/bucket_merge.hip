@@ -21,11 +21,13 @@ constexpr int kBucketLdsBins = 8192;  // LDS histogram limit (heads x past block
 // read in memory order (consecutive lanes take consecutive rows, so a wave
 // reads one contiguous range per token), counted into an LDS histogram per
 // (head of the group, past block) and flushed with one global atomic per
-// touched bin.
+// touched bin.  Dense-prefix rows (dense_row) are skipped; a row below
+// dense_blocks that is not one marks its (head, own block) in notfull.
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int tile_tokens,
-    int H, int h0, int HC, int NB, int block_size, int topk, int32_t* __restrict__ counts) {
+    int H, int h0, int HC, int NB, int block_size, int topk, int dense_blocks,
+    int32_t* __restrict__ counts, int32_t* __restrict__ notfull) {
   __shared__ int32_t hist[kBucketLdsBins];
   const int sid = blockIdx.x / tiles_per_seq;
   const int tile = blockIdx.x % tiles_per_seq;
@@ -51,6 +53,10 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int h = r - (r / HC) * HC;
     const int c = p / block_size;
     const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * topk;
+    if (c < dense_blocks) {
+      if (dense_row(row, topk, c, dense_blocks)) return;
+      if (gb0 + c < NB) notfull[(size_t)h * NB + gb0 + c] = 1;
+    }
     int last = -1, nh = 0;
     auto visit = [&](int e) {
       if (accept_hist(e, c, last, nh, topk)) {
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int nunits,
     int tile_tokens, int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
-    int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    int dense_blocks, int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ list) {
   __shared__ int32_t hist[kScatterBins];
   __shared__ int32_t loff[kScatterBins + 1];
@@ -142,6 +148,7 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
   auto walk = [&](int p, auto&& f) {
     const int c = p / block_size;
     const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + hl) * topk;
+    if (dense_row(row, topk, c, dense_blocks)) return;
     int last = -1, nh = 0;
     auto visit = [&](int e) {
       if (accept_hist(e, c, last, nh, topk)) {
@@ -279,12 +286,15 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
                          int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st,
-                         bool tokens_only) {
+                         bool tokens_only, int dense_blocks, int32_t* notfull) {
   const int slot_stride = tokens_only ? 0 : topk;
   const int n = g.head_cnt * g.total_blocks;
   if (n > 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
                        counts, n);
+    if (dense_blocks > 0)
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(min(1024, (n + 255) / 256)), dim3(256), 0, st,
+                         notfull, n);
   }
   // tiles of 32..256 tokens, small enough for about 1024 workgroups
   int tile_tokens = kBucketTokensMax;
@@ -294,7 +304,8 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
   if (tiles > 0 && topk > 1)
     hipLaunchKernelGGL(bucket_count_kernel, grid, dim3(256), 0, st, block_idx, g.cu_seqlens,
                        g.cu_blocks, g.total_tokens, tiles, tile_tokens, g.num_heads, g.head_lo,
-                       g.head_cnt, g.total_blocks, g.block_size, topk, counts);
+                       g.head_cnt, g.total_blocks, g.block_size, topk, dense_blocks, counts,
+                       notfull);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, st, counts, n, tile_q,
                      offsets, tile_offsets);
   if (tiles > 0 && topk > 1) {
@@ -306,7 +317,7 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
                        block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, stiles, nunits, rt,
                        g.num_heads, g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk,
-                       slot_stride, counts, offsets, list);
+                       slot_stride, dense_blocks, counts, offsets, list);
   }
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,
@@ -436,7 +447,7 @@ template <int D, bool kPartF16, bool kOutBf16>
 __global__ __launch_bounds__(256) void merge_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     int num_seqs, int total_tokens, int H, int h0, int HC, int block_size, int topk,
-    const void* __restrict__ o_part, const float* __restrict__ lse_part,
+    int dense_blocks, const void* __restrict__ o_part, const float* __restrict__ lse_part,
     const uint32_t* __restrict__ vmax_bits, void* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 16;  // output dims per lane
   __shared__ float wts[16][64];
@@ -450,10 +461,12 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const long long grow = (long long)t * H + h0 + hl;       // (token, global head)
   int nparts = 0;
   float tot = 0.f;
+  bool dense = false;  // written by the dense-prefix pass
   if (valid) {
     const int s = upper_index(cu_seqlens, num_seqs, t);
     const int c = (t - cu_seqlens[s]) / block_size;
     const int nh = count_hist(block_idx + grow * topk, topk, c);
+    dense = c < dense_blocks && nh == c;
     nparts = nh + 1;
     // part i < nh lives in slot i; the own block in slot topk - 1
     float l4[4];
@@ -479,7 +492,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
     }
   }
   __syncthreads();
-  if (!valid) return;
+  if (!valid || dense) return;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
@@ -557,16 +570,18 @@ __global__ __launch_bounds__(256) void merge_kernel(
   if (li == 0) lse[grow] = tot;
 }
 
-hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
-                        bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
-                        void* out, bool out_bf16, float* lse, hipStream_t st) {
+hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, int dense_blocks,
+                        const void* o_part, bool part_f16, const float* lse_part,
+                        const uint32_t* vmax_bits, void* out, bool out_bf16, float* lse,
+                        hipStream_t st) {
   const long long rows = (long long)g.total_tokens * g.head_cnt;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
 #define MOBA_MERGE(D, PB, OB)                                                            \
   hipLaunchKernelGGL((merge_kernel<D, PB, OB>), grid, dim3(256), 0, st, block_idx,       \
                      g.cu_seqlens, g.num_seqs, g.total_tokens, g.num_heads, g.head_lo,    \
-                     g.head_cnt, g.block_size, topk, o_part, lse_part, vmax_bits, out, lse)
+                     g.head_cnt, g.block_size, topk, dense_blocks, o_part, lse_part, vmax_bits, \
+                     out, lse)
   if (g.head_dim == 128) {
     if (part_f16) { if (out_bf16) MOBA_MERGE(128, true, true); else MOBA_MERGE(128, true, false); }
     else { if (out_bf16) MOBA_MERGE(128, false, true); else MOBA_MERGE(128, false, false); }

@@ -133,6 +133,15 @@ __device__ __forceinline__ int count_hist(const int32_t* __restrict__ row, int t
   return nh;
 }
 
+// A row whose own block c is below dense_blocks and that selects every past
+// block 0 .. c - 1 attends to its whole causal prefix [0, t]: the forward's
+// dense-prefix pass writes it, and the bucketing, own-block and merge passes
+// skip it (dense_blocks 0: no such rows).
+__device__ __forceinline__ bool dense_row(const int32_t* __restrict__ row, int topk, int c,
+                                          int dense_blocks) {
+  return c < dense_blocks && count_hist(row, topk, c) == c;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2): workgroup b runs on XCD b % 8.  xcd_remap(b, n) gives workgroup b the
 // work item that makes every XCD process one contiguous share of [0, n), so

@@ -54,7 +54,8 @@ inline int hist_tile_q(int block_size, int head_dim) {
 
 // Workspace carve-up of moba_attn_fwd (offsets in bytes, 256-aligned).
 struct AttnWorkspace {
-  size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, tile_info, vmax, total;
+  size_t counts, offsets, tile_offsets, list, lse_part, o_part, vt, tile_info, vmax, notfull,
+      total;
 };
 AttnWorkspace attn_workspace_layout(bool bf16, long long total_tokens, long long total_blocks,
                                     long long num_heads, long long head_dim,
@@ -80,10 +81,14 @@ hipError_t launch_static_select(const Geo& g, int topk, int sink, int32_t* block
 // With tile_info, also writes {key, first entry, end entry, 0} for each of
 // the max_tiles tiles of tile_q rows (key -1 past the last tile).
 // List entries are token * topk + slot, or (tokens_only) the global token.
+// dense_blocks > 0: rows of the dense prefix (dense_row in common.h) get no
+// entries, and notfull[head of the group, global block] is set to 1 for
+// every block below dense_blocks holding a row that is not one.
 hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int tile_q,
                          int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
                          int32_t* list, int4* tile_info, long long max_tiles, hipStream_t st,
-                         bool tokens_only = false);
+                         bool tokens_only = false, int dense_blocks = 0,
+                         int32_t* notfull = nullptr);
 
 // Transposed, key-permuted fp16 copy of V per (block, head) for the MFMA
 // kernels, scaled per head by 2^-e (vmax_bits[h] receives max |v|).
@@ -97,12 +102,25 @@ hipError_t launch_attn_mfma_hist(const void* q, const void* k, const uint16_t* v
                                  const Geo& g, int topk, float scale, const int32_t* list,
                                  const int4* tile_info, long long max_tiles, uint16_t* o_part,
                                  float* lse_part, hipStream_t st);
+// own: blocks below dense_blocks whose notfull flag is 0 hold only
+// dense-prefix rows and are skipped.  dense: queries at local positions
+// below q_limit only (the dense prefix of each sequence; INT_MAX: all).
 hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt,
                                 const Geo& g, int topk, float scale, uint16_t* o_part,
-                                float* lse_part, hipStream_t st);
+                                float* lse_part, int dense_blocks, const int32_t* notfull,
+                                hipStream_t st);
+// Workgroups of a dense launch over the first q_limit positions of each
+// sequence (every sequence padded to the longest one).
+inline long long dense_grid(const Geo& g, int q_limit) {
+  const int span = q_limit < g.max_seqlen ? q_limit : g.max_seqlen;
+  if (span <= 0) return 0;
+  const int tq = mfma_tile_q(span);
+  return (long long)((span + tq - 1) / tq) * g.num_seqs * g.head_cnt;
+}
 hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
                                   const uint32_t* vmax_bits, const Geo& g, float scale,
-                                  void* out, bool out_bf16, float* lse, hipStream_t st);
+                                  void* out, bool out_bf16, float* lse, hipStream_t st,
+                                  int q_limit = 0x7fffffff);
 
 // fp32 VALU attention (one wave per query row and key range).
 hipError_t launch_attn_f32_hist(const float* q, const float* k, const float* v, const Geo& g,
@@ -116,10 +134,12 @@ hipError_t launch_attn_f32_dense(const float* q, const float* k, const float* v,
                                  float scale, void* out, bool out_bf16, float* lse,
                                  hipStream_t st);
 
-// Online-softmax combine of the partials of every (token, head) row.
-hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, const void* o_part,
-                        bool part_f16, const float* lse_part, const uint32_t* vmax_bits,
-                        void* out, bool out_bf16, float* lse, hipStream_t st);
+// Online-softmax combine of the partials of every (token, head) row (rows of
+// the dense prefix excepted when dense_blocks > 0).
+hipError_t launch_merge(const int32_t* block_idx, const Geo& g, int topk, int dense_blocks,
+                        const void* o_part, bool part_f16, const float* lse_part,
+                        const uint32_t* vmax_bits, void* out, bool out_bf16, float* lse,
+                        hipStream_t st);
 
 // Backward: Dq = rowsum(dO * O) and dq = 0; dK, dV per (head, block, 128
 // keys) over the block's list and own-block queries; dQ over the forward's

@@ -260,6 +260,90 @@ def test_moba_edge_cases(dev, w):
     print(w.name, st)
 
 
+def _stages(fn):
+    """Names of the library stages that fn() launches."""
+    prof = moba.Profiler().attach()
+    try:
+        prof.reset()
+        fn()
+        torch.cuda.synchronize()
+        return set(prof.names())
+    finally:
+        prof.detach()
+        prof.close()
+
+
+@pytest.mark.parametrize("w", [
+    # 6 query tiles of 128 x 3 sequences x 16 heads: a dense-prefix launch of
+    # 288 workgroups
+    inputs.custom([3000, 1700, 600], 16, 128, 128, 6, "bf16", name="prefix-B128-k6"),
+    # 12 tiles of 256 x 2 sequences x 12 heads
+    inputs.custom([5000, 2100], 12, 64, 1024, 3, "bf16", name="prefix-d64-B1024-k3"),
+], ids=lambda w: w.name)
+def test_prefix_rows_missing_blocks(dev, w):
+    """Rows of the first k blocks normally select every earlier block and are
+    computed as dense causal rows.  Here a given selection drops one past
+    block from some of them (odd rows of blocks 2 and 4 of each sequence,
+    every row of block 1 of the first sequence), so blocks hold both kinds
+    of rows.  Every prefix row and a sample of the others, on three heads,
+    are checked against the oracle on the selection actually passed, and the
+    result is compared with a run in passes of 4 heads, whose prefix launch
+    would be too small to be used (every row bucketed)."""
+    _say(w.name, w.seqlens, "H", w.heads, "d", w.head_dim, "B", w.block_size, "k", w.topk)
+    x = inputs.make_inputs(w, device=dev, seed=31)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    _, _, idx = moba.forward(x["q"], x["k"], x["v"], geom, w.topk, w.scale)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy().copy()
+    cu = x["cu_seqlens"]
+    rng = np.random.default_rng(8)
+    changed = 0
+    for s in range(len(w.seqlens)):
+        a, L = cu[s], cu[s + 1] - cu[s]
+        for p in range(min(L, w.topk * w.block_size)):
+            c = p // w.block_size
+            drop = (c in (2, 4) and p % 2 == 1) or (s == 0 and c == 1)
+            if c == 0 or not drop:
+                continue
+            for h in range(w.heads):
+                row = [e for e in sel[a + p, h] if e >= 0]
+                assert row == list(range(c + 1)), row  # full prefix from the gate
+                del row[int(rng.integers(0, c))]
+                sel[a + p, h] = row + [-1] * (w.topk - len(row))
+                changed += 1
+    assert changed > 0
+    block_idx = torch.as_tensor(sel, device=dev)
+    res = {}
+
+    def run(chunk):
+        res[chunk] = moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, w.topk, block_idx,
+                                        w.scale, out_dtype=torch.float32, head_chunk=chunk)
+
+    assert "attn_prefix" in _stages(lambda: run(0))
+    assert "attn_prefix" not in _stages(lambda: run(4))
+    out, lse = res[0]
+    prefix = [cu[s] + p for s in range(len(w.seqlens))
+              for p in range(min(cu[s + 1] - cu[s], w.topk * w.block_size))]
+    rest = np.setdiff1d(np.arange(w.total_tokens), prefix)
+    rest = rng.choice(rest, min(len(rest), 400), replace=False)
+    toks = np.sort(np.concatenate([np.asarray(prefix, dtype=np.int64), rest]))
+    stats = []
+    for h in (0, w.heads // 2, w.heads - 1):
+        rows_h = np.stack([toks, np.zeros_like(toks)], axis=1)
+        o_ref, l_ref = mo.attend_given_selection(
+            parity.host_head(x["q"], h), parity.host_head(x["k"], h), parity.host_head(x["v"], h),
+            cu, w.block_size, sel[toks, h].astype(np.int64), w.scale, rows_h)
+        tt = torch.as_tensor(toks, device=dev)
+        st = parity.error_stats(out[tt, h].cpu().numpy(), o_ref, lse[tt, h].cpu().numpy(), l_ref)
+        parity.assert_within(st, parity.BF16_TOL, f"{w.name} head {h}")
+        stats.append(st)
+    o4, l4 = res[4]
+    # two bf16-MFMA evaluations of the same rows, different rounding order
+    assert (out - o4).abs().max().item() < 1e-2
+    assert (lse - l4).abs().max().item() < 1e-3
+    print(w.name, "changed rows", changed, stats)
+
+
 def test_moba_peaky_softmax(dev):
     """Sharp attention (queries scaled by 4, scores of std ~4): a few keys
     dominate each softmax, the regime where rounding of the probabilities
@@ -327,17 +411,31 @@ def test_deterministic(dev):
     assert torch.equal(lse1, lse2)
 
 
-def test_bucket_lists_rebuild_selection(dev):
-    """The per-block query lists hold exactly the historical selections."""
-    w = inputs.custom([3000, 1100], 2, 128, 128, 5, "bf16", name="lists")
+@pytest.mark.parametrize("heads", [2, 32])
+def test_bucket_lists_rebuild_selection(dev, heads):
+    """The per-block query lists hold exactly the historical selections.
+    With 32 heads the dense-prefix launch fills the chip, so rows of the
+    first k blocks that select every earlier block (each such row under the
+    gate) are computed by the dense kernel and have no list entries; with 2
+    heads that launch would be too small and every row is bucketed."""
+    w = inputs.custom([3000, 1100], heads, 128, 128, 5, "bf16", name="lists")
+    _say(w.name, w.seqlens, "H", heads, "B", w.block_size, "k", w.topk)
     x = inputs.make_inputs(w, device=dev, seed=4)
     geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
     out, lse, idx = moba.forward(x["q"], x["k"], x["v"], geom, w.topk, w.scale)
     ws = torch.empty(moba.moba_attn_workspace_bytes(moba.MOBA_BF16, geom.total_tokens,
                                                     geom.total_blocks, w.heads, 128, 128, 5, 0),
                      dtype=torch.uint8, device=dev)
-    moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, w.topk, idx, w.scale, workspace=ws)
-    torch.cuda.synchronize()
+    prof = moba.Profiler().attach()
+    try:
+        prof.reset()
+        moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, w.topk, idx, w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        prefix_route = "attn_prefix" in prof.names()
+    finally:
+        prof.detach()
+        prof.close()
+    assert prefix_route == (heads == 32)
     H, NB, k, T = w.heads, geom.total_blocks, w.topk, geom.total_tokens
     al = lambda n: (n + 255) // 256 * 256
     off_counts = 0
@@ -361,6 +459,9 @@ def test_bucket_lists_rebuild_selection(dev):
         c = (t - cu[s]) // w.block_size
         for h in range(H):
             row = [int(v) for v in idx_h[t, h] if 0 <= v < c]
+            if prefix_route and c < k:
+                assert row == list(range(c))
+                continue
             for slot, b in enumerate(row):
                 want.add((t, h, slot, int(cb[s] + b)))
     assert got == want
