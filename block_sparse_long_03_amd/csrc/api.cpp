@@ -224,9 +224,10 @@ namespace {
 // earlier block (all of them under the gate) attend to their whole causal
 // prefix, so the dense kernel writes them directly (stage "attn_prefix") and
 // bucketing, the own-block pass and the merge skip them.  This route is taken
-// when the prefix launch fills the chip (kPrefixMinGrid workgroups): a
-// smaller one runs for as long as its heaviest tile (topk * block_size keys)
-// takes, longer than the passes it saves.
+// when the prefix launch over all heads fills the chip (kPrefixMinGrid
+// workgroups): a smaller one runs for as long as its heaviest tile (topk *
+// block_size keys) takes, longer than the passes it saves.  The choice does
+// not depend on the head passes, so neither do the results.
 moba_status attn_pass(const void* q, const void* k, const void* v, bool bf16, const moba::Geo& g,
                       int topk, const int32_t* block_idx, float softmax_scale, void* out,
                       int out_dtype, float* lse, char* ws, const moba::AttnWorkspace& L,

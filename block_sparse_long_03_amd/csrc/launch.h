@@ -110,12 +110,14 @@ hipError_t launch_attn_mfma_own(const void* q, const void* k, const uint16_t* vt
                                 float* lse_part, int dense_blocks, const int32_t* notfull,
                                 hipStream_t st);
 // Workgroups of a dense launch over the first q_limit positions of each
-// sequence (every sequence padded to the longest one).
+// sequence (every sequence padded to the longest one) and all num_heads
+// heads.  It depends on the layer's geometry only, not on how the heads are
+// split into passes, so a choice made from it is the same for every split.
 inline long long dense_grid(const Geo& g, int q_limit) {
   const int span = q_limit < g.max_seqlen ? q_limit : g.max_seqlen;
   if (span <= 0) return 0;
   const int tq = mfma_tile_q(span);
-  return (long long)((span + tq - 1) / tq) * g.num_seqs * g.head_cnt;
+  return (long long)((span + tq - 1) / tq) * g.num_seqs * g.num_heads;
 }
 hipError_t launch_attn_mfma_dense(const void* q, const void* k, const uint16_t* vt,
                                   const uint32_t* vmax_bits, const Geo& g, float scale,
