@@ -248,6 +248,7 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     dt = moba.MOBA_BF16 if w.dtype == "bf16" else moba.MOBA_F32
     kbar = torch.empty((geom.total_blocks, H, 2 if gate == "minmax" else 1, d),
                        dtype=torch.float32, device=dev)
+    kbar3 = torch.empty((H, 3, d // 16, geom.total_blocks, 16), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((geom.total_tokens, H, w.topk), dtype=torch.int32, device=dev)
     out = torch.empty_like(x["q"])
     lse = torch.empty((geom.total_tokens, H), dtype=torch.float32, device=dev)
@@ -258,8 +259,8 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
 
     def step():
         if gate == "mean":
-            moba.moba_pool_keys(k, geom, kbar=kbar)
-            moba.moba_gate_topk(q, kbar, geom, w.topk, block_idx=idx)
+            pooled = moba.moba_pool_keys(k, geom, kbar=kbar, kbar3=kbar3)
+            moba.moba_gate_topk(q, pooled, geom, w.topk, block_idx=idx)
         elif gate == "minmax":
             moba.moba_pool_minmax(k, geom, kminmax=kbar)
             moba.moba_gate_topk_minmax(q, kbar, geom, w.topk, block_idx=idx)
@@ -317,7 +318,7 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     prof.detach()
     prof.close()
     lengths = list_lengths(torch, idx, w.seqlens, w.block_size) if w.dtype == "bf16" else None
-    del kbar, idx, out, lse
+    del kbar, kbar3, idx, out, lse
     if not keep:
         del x, q, k, v
         x = None

@@ -326,7 +326,7 @@ int moba_last_hip_error(void) { return g_last_hip_error; }
 moba_status moba_pool_keys(const void* k, int dtype, const int32_t* cu_seqlens,
                            const int32_t* cu_blocks, int num_seqs, int total_tokens,
                            int max_seqlen, int total_blocks, int num_heads, int head_dim,
-                           int block_size, float* kbar, void* stream) {
+                           int block_size, float* kbar, uint16_t* kbar3, void* stream) {
   moba_status st = check_geometry(dtype, cu_seqlens, cu_blocks, num_seqs, total_tokens,
                                   max_seqlen, total_blocks, num_heads, head_dim, block_size);
   if (st != MOBA_OK) return st;
@@ -335,13 +335,14 @@ moba_status moba_pool_keys(const void* k, int dtype, const int32_t* cu_seqlens,
   moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
                          total_blocks, num_heads, head_dim, block_size);
   hipError_t e = timed("pool_keys", (hipStream_t)stream, [&] {
-    return moba::launch_pool_keys(k, dtype == MOBA_BF16, g, kbar, (hipStream_t)stream);
+    return moba::launch_pool_keys(k, dtype == MOBA_BF16, g, kbar, kbar3, (hipStream_t)stream);
   });
   return e == hipSuccess ? MOBA_OK : hip_fail(e);
 }
 
 moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
-                           const int32_t* cu_seqlens, const int32_t* cu_blocks, int num_seqs,
+                           const uint16_t* kbar3, const int32_t* cu_seqlens,
+                           const int32_t* cu_blocks, int num_seqs,
                            int total_tokens, int max_seqlen, int total_blocks, int num_heads,
                            int head_dim, int block_size, int topk, int32_t* block_idx,
                            void* stream) {
@@ -351,11 +352,12 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
   st = check_topk(total_tokens, topk);
   if (st != MOBA_OK) return st;
   if (total_tokens == 0) return MOBA_OK;
-  if (!q || !kbar || !block_idx) return MOBA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == MOBA_BF16;
+  if (!q || !block_idx || (bf16 ? !kbar3 : !kbar)) return MOBA_ERR_INVALID_ARG;
   moba::Geo g = make_geo(cu_seqlens, cu_blocks, num_seqs, total_tokens, max_seqlen,
                          total_blocks, num_heads, head_dim, block_size);
   hipError_t e = timed("gate_topk", (hipStream_t)stream, [&] {
-    return moba::launch_gate_topk(q, dtype == MOBA_BF16, kbar, g, topk, block_idx,
+    return moba::launch_gate_topk(q, bf16, kbar, kbar3, g, topk, block_idx,
                                   (hipStream_t)stream);
   });
   return e == hipSuccess ? MOBA_OK : hip_fail(e);

@@ -67,9 +67,12 @@ long long hist_tiles_bound(long long total_tokens, long long total_blocks, long 
 size_t dense_workspace_bytes(bool bf16, long long total_blocks, long long num_heads,
                              long long head_dim, long long block_size);
 
-hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar, hipStream_t st);
-hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const Geo& g,
-                            int topk, int32_t* block_idx, hipStream_t st);
+// kbar3 (optional): the means as hi + mid + lo bf16 planes [block, head, 3, d]
+hipError_t launch_pool_keys(const void* k, bool bf16, const Geo& g, float* kbar,
+                            uint16_t* kbar3, hipStream_t st);
+// bf16 queries score against kbar3, fp32 queries against kbar
+hipError_t launch_gate_topk(const void* q, bool bf16, const float* kbar, const uint16_t* kbar3,
+                            const Geo& g, int topk, int32_t* block_idx, hipStream_t st);
 hipError_t launch_pool_minmax(const void* k, bool bf16, const Geo& g, float* kmm, hipStream_t st);
 hipError_t launch_gate_topk_minmax(const uint16_t* q, const float* kmm, const Geo& g, int topk,
                                    int32_t* block_idx, hipStream_t st);

@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from typing import NamedTuple
 
 import torch
 
@@ -27,7 +28,7 @@ MOBA_ERR_HIP = -4
 MOBA_F32 = 0
 MOBA_BF16 = 1
 # the MOBA_API_VERSION of include/moba.h these bindings are written for
-API_VERSION = 4
+API_VERSION = 5
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
@@ -67,9 +68,9 @@ def lib():
     L.moba_last_hip_error.restype = i32
     L.moba_last_hip_error.argtypes = []
     L.moba_pool_keys.restype = i32
-    L.moba_pool_keys.argtypes = [vp, i32] + geo + [vp, vp]
+    L.moba_pool_keys.argtypes = [vp, i32] + geo + [vp, vp, vp]
     L.moba_gate_topk.restype = i32
-    L.moba_gate_topk.argtypes = [vp, i32, vp] + geo + [i32, vp, vp]
+    L.moba_gate_topk.argtypes = [vp, i32, vp, vp] + geo + [i32, vp, vp]
     L.moba_pool_minmax.restype = i32
     L.moba_pool_minmax.argtypes = [vp, i32] + geo + [vp, vp]
     L.moba_gate_topk_minmax.restype = i32
@@ -178,22 +179,41 @@ def _qkv_shape(x, geom):
     return x.shape[1], x.shape[2]
 
 
-def moba_pool_keys(k, geom, kbar=None, stream=None):
+class PooledKeys(NamedTuple):
+    """Output of moba_pool_keys: kbar [NB, H, d] fp32 means and kbar3
+    [H, 3, d / 16, NB, 16] bf16, the same means as exact hi + mid + lo terms
+    (``kbar3_terms`` gives them as [NB, H, 3, d])."""
+    kbar: torch.Tensor
+    kbar3: torch.Tensor
+
+
+def moba_pool_keys(k, geom, kbar=None, kbar3=None, stream=None):
     H, d = _qkv_shape(k, geom)
     if kbar is None:
         kbar = torch.empty((geom.total_blocks, H, d), dtype=torch.float32, device=k.device)
+    if kbar3 is None:
+        kbar3 = torch.empty((H, 3, d // 16, geom.total_blocks, 16), dtype=torch.bfloat16,
+                            device=k.device)
     _check("moba_pool_keys", lib().moba_pool_keys(
-        _ptr(k), _dtype_code(k.dtype), *geom.args(H, d), _ptr(kbar), _stream(stream)))
-    return kbar
+        _ptr(k), _dtype_code(k.dtype), *geom.args(H, d), _ptr(kbar), _ptr(kbar3),
+        _stream(stream)))
+    return PooledKeys(kbar, kbar3)
 
 
-def moba_gate_topk(q, kbar, geom, topk, block_idx=None, stream=None):
+def kbar3_terms(kbar3, num_heads, head_dim, total_blocks):
+    """[NB, H, 3, d] view order of a kbar3 buffer (a copy)."""
+    t = kbar3.reshape(num_heads, 3, head_dim // 16, total_blocks, 16)
+    return t.permute(3, 0, 1, 2, 4).reshape(total_blocks, num_heads, 3, head_dim)
+
+
+def moba_gate_topk(q, pooled, geom, topk, block_idx=None, stream=None):
+    """pooled: the PooledKeys of moba_pool_keys."""
     H, d = _qkv_shape(q, geom)
     if block_idx is None:
         block_idx = torch.empty((geom.total_tokens, H, topk), dtype=torch.int32, device=q.device)
     _check("moba_gate_topk", lib().moba_gate_topk(
-        _ptr(q), _dtype_code(q.dtype), _ptr(kbar), *geom.args(H, d), int(topk),
-        _ptr(block_idx), _stream(stream)))
+        _ptr(q), _dtype_code(q.dtype), _ptr(pooled.kbar), _ptr(pooled.kbar3),
+        *geom.args(H, d), int(topk), _ptr(block_idx), _stream(stream)))
     return block_idx
 
 
@@ -352,8 +372,8 @@ def forward(q, k, v, geom, topk, scale, out_dtype=None, workspace=None, stream=N
             head_chunk=0):
     """MoBA prefill forward: pool -> gate/top-k -> sparse attention.
     Returns (out, lse, block_idx)."""
-    kbar = moba_pool_keys(k, geom, stream=stream)
-    idx = moba_gate_topk(q, kbar, geom, topk, stream=stream)
+    pooled = moba_pool_keys(k, geom, stream=stream)
+    idx = moba_gate_topk(q, pooled, geom, topk, stream=stream)
     out, lse = moba_attn_fwd(q, k, v, geom, topk, idx, scale, out_dtype=out_dtype,
                              workspace=workspace, stream=stream, head_chunk=head_chunk)
     return out, lse, idx

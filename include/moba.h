@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOBA_API_VERSION 4
+#define MOBA_API_VERSION 5
 
 /* Size of the device workspace moba_attn_fwd_static keeps inside the library
  * (per GPU, for the life of the process). */
@@ -92,15 +92,27 @@ int moba_last_hip_error(void);
  * Defined by the mean_pool(K[I_i]) of the affinity in "MoBA: Learned Block
  * Sparsity for Long-Context Attention", section "The Change", and step 2 of
  * "MoBA: 面向长上下文大语言模型的混合块注意力机制" (技术实现).
- *   k     [total_tokens, num_heads, head_dim], dtype
- *   kbar  [total_blocks, num_heads, head_dim] fp32, written in full
+ *   k      [total_tokens, num_heads, head_dim], dtype
+ *   kbar   [total_blocks, num_heads, head_dim] fp32, written in full
+ *   kbar3  bf16 bit patterns, total_blocks * num_heads * 3 * head_dim of
+ *          them, or NULL (not written): the same means as an exact sum of
+ *          three bf16 terms, kbar = hi + mid + lo, where hi is the upper half
+ *          of kbar's fp32 pattern, mid the upper half of kbar - hi and lo the
+ *          (exactly representable) rest.  Layout [num_heads][3 terms]
+ *          [head_dim / 16][total_blocks][16]: term x of element e of block b,
+ *          head h sits at ((h * 3 + x) * (head_dim / 16) + e / 16) *
+ *          total_blocks * 16 + b * 16 + e % 16.  This is the form in which
+ *          the bf16 gate reads the pooled keys: three exact bf16 products per
+ *          element on the matrix cores give the fp32 score, and one load
+ *          reads the k-step fragments of 32 consecutive blocks at once.
+ *          (Exact for means of magnitude 2^-110 or more.)
  * Summation is fp32 in a fixed order (deterministic).
  */
 moba_status moba_pool_keys(const void* k, int dtype,
                            const int32_t* cu_seqlens, const int32_t* cu_blocks,
                            int num_seqs, int total_tokens, int max_seqlen,
                            int total_blocks, int num_heads, int head_dim,
-                           int block_size, float* kbar, void* stream);
+                           int block_size, float* kbar, uint16_t* kbar3, void* stream);
 
 /*
  * Gate and causal top-k selection.
@@ -113,14 +125,17 @@ moba_status moba_pool_keys(const void* k, int dtype,
  * "MoBA: Learned Block Sparsity for Long-Context Attention", section "The
  * Change" (affinity, hard top-k gate, causality rules).
  *   q          [total_tokens, num_heads, head_dim], dtype
- *   kbar       output of moba_pool_keys
+ *   kbar       output of moba_pool_keys; read for fp32 queries
+ *   kbar3      its three-term bf16 form from moba_pool_keys; read for bf16
+ *              queries (required then; may be NULL for fp32)
  *   block_idx  [total_tokens, num_heads, topk] int32, written in full: the
  *              selected local block ids in ascending order (so the own block
  *              is the last valid entry), then -1 padding
  * Scores are fp32 (fp32 products of the exact inputs, fp32 accumulation).
  */
 moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
-                           const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                           const uint16_t* kbar3, const int32_t* cu_seqlens,
+                           const int32_t* cu_blocks,
                            int num_seqs, int total_tokens, int max_seqlen,
                            int total_blocks, int num_heads, int head_dim,
                            int block_size, int topk, int32_t* block_idx,

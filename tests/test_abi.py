@@ -54,7 +54,7 @@ def pool(L, **kw):
     g = dict(GEO, **kw)
     return L.moba_pool_keys(kw.get("k", FAKE), kw.get("dtype", 1), g["cu"], g["cb"], g["S"],
                             g["T"], g["maxL"], g["NB"], g["H"], g["d"], g["B"],
-                            kw.get("kbar", FAKE), None)
+                            kw.get("kbar", FAKE), kw.get("kbar3", None), None)
 
 
 def attn(L, topk=3, scale=0.1, ws=FAKE, ws_bytes=1 << 40, out_dtype=1, head_chunk=0, **kw):
@@ -110,6 +110,17 @@ def test_static_select_arguments(L):
     assert static(L, topk=65) == U
     assert static(L, B=96) == U
     assert static(L, T=0, maxL=0, NB=0, idx=None) == moba.MOBA_OK   # empty batch: nothing to do
+
+
+def test_gate_arguments(L):
+    # bf16 queries read the three-term pooled keys, fp32 queries the fp32 means
+    E = moba.MOBA_ERR_INVALID_ARG
+    g = [GEO[x] for x in ("cu", "cb", "S", "T", "maxL", "NB", "H", "d", "B")]
+    assert L.moba_gate_topk(FAKE, 1, FAKE, None, *g, 3, FAKE, None) == E
+    assert L.moba_gate_topk(FAKE, 0, None, FAKE, *g, 3, FAKE, None) == E
+    assert L.moba_gate_topk(None, 1, FAKE, FAKE, *g, 3, FAKE, None) == E
+    assert L.moba_gate_topk(FAKE, 1, FAKE, FAKE, *g, 3, None, None) == E
+    assert L.moba_gate_topk(FAKE, 1, FAKE, FAKE, *g, 0, FAKE, None) == E
 
 
 def test_minmax_arguments(L):

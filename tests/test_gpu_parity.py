@@ -53,7 +53,15 @@ def test_pool_keys(dev, w):
     _say("pool", w.name)
     x = inputs.make_inputs(w, device=dev)
     geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
-    kbar = moba.moba_pool_keys(x["k"], geom).cpu().numpy()
+    pooled = moba.moba_pool_keys(x["k"], geom)
+    kbar = pooled.kbar.cpu().numpy()
+    # the three bf16 terms add up to the fp32 means exactly, hi being the
+    # upper half of the fp32 pattern
+    NB, H, d = pooled.kbar.shape
+    k3 = moba.kbar3_terms(pooled.kbar3, H, d, NB).float()
+    assert torch.equal((k3[:, :, 0] + k3[:, :, 1]) + k3[:, :, 2], pooled.kbar)
+    bits = pooled.kbar.contiguous().view(torch.int32)
+    assert torch.equal(k3[:, :, 0].contiguous().view(torch.int32), bits & -65536)
     ref = mo.pool_keys(x["k"].float().cpu().numpy(), x["cu_seqlens"], w.block_size)
     assert kbar.shape == ref.shape
     np.testing.assert_allclose(kbar, ref, rtol=0, atol=2e-6 * max(1.0, np.abs(ref).max()))
@@ -98,6 +106,41 @@ def test_gate_topk_spans(dev, w):
     idx = moba.moba_gate_topk(x["q"], moba.moba_pool_keys(x["k"], geom), geom, w.topk)
     st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx)
     print(w.name, st)
+
+
+@pytest.mark.parametrize("k", [4, 12, 21, 33])
+def test_gate_topk_exact_ties(dev, k):
+    """Exact ties: in each sequence, blocks 2, 5, 9, ... repeat the keys of
+    block 1 (equal pooled keys, so bitwise equal scores), and every third
+    query is zero (all its scores are 0: every past block ties, more
+    candidates than the candidate selection takes, so those waves select row
+    by row).  The lower block index wins every tie: on rows whose boundary
+    is an exact tie the selection must equal the oracle's; other rows follow
+    the usual near-tie rule."""
+    B = 64
+    w = inputs.custom([B * 40 + 17, B * 20, B * 300 + 3], 2, 128, B, k, "bf16",
+                      name=f"gate-ties-k{k}")
+    _say("gate ties", w.seqlens, "k", k)
+    x = inputs.make_inputs(w, device=dev, seed=9)
+    cu = x["cu_seqlens"]
+    for s in range(len(w.seqlens)):
+        a, L = cu[s], cu[s + 1] - cu[s]
+        for b in (2, 5, 9, 13, 17, 21, 29, 33, 100, 257, 290):
+            if (b + 1) * B <= L:
+                x["k"][a + b * B:a + (b + 1) * B] = x["k"][a + B:a + 2 * B]
+    x["q"][0::3] = 0
+    geom = moba.Geometry.make(cu, B, dev)
+    idx = moba.moba_gate_topk(x["q"], moba.moba_pool_keys(x["k"], geom), geom, k)
+    torch.cuda.synchronize()
+    qn, kn = x["q"].float().cpu().numpy(), x["k"].float().cpu().numpy()
+    ref = mo.gate_reference(qn, kn, cu, B, k)
+    rows = ref["rows"]
+    gi = idx.cpu().numpy()[rows[:, 0], rows[:, 1]].astype(np.int64)
+    exact = ref["gap"] == 0
+    assert exact.sum() > 1000
+    assert np.array_equal(gi[exact], ref["idx"][exact])
+    st = parity.check_idx_all_rows(x["q"], x["k"], cu, B, k, idx)
+    print(w.name, "exact-tie rows", int(exact.sum()), st)
 
 
 # ---------------------------------------------------------------------------

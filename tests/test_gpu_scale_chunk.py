@@ -215,13 +215,16 @@ def test_guard_bands(dev, w, hc):
     nbytes = moba.moba_attn_workspace_bytes(moba._dtype_code(dt), T, geom.total_blocks, H, d,
                                             w.block_size, k, hc)
     w_buf, ws = _guarded(nbytes, torch.uint8, dev, 0xA5)
-    moba.moba_pool_keys(x["k"], geom, kbar=kbar.view(geom.total_blocks, H, d))
-    moba.moba_gate_topk(x["q"], kbar.view(geom.total_blocks, H, d), geom, k,
+    k3_buf, kbar3 = _guarded(geom.total_blocks * H * 3 * d, torch.bfloat16, dev, 0x7FBF)
+    pooled = moba.moba_pool_keys(x["k"], geom, kbar=kbar.view(geom.total_blocks, H, d),
+                                 kbar3=kbar3.view(H, 3, d // 16, geom.total_blocks, 16))
+    moba.moba_gate_topk(x["q"], pooled, geom, k,
                         block_idx=idx.view(T, H, k))
     moba.moba_attn_fwd(x["q"], x["k"], x["v"], geom, k, idx.view(T, H, k), w.scale,
                        out=out.view(T, H, d), lse=lse.view(T, H), workspace=ws, head_chunk=hc)
     torch.cuda.synchronize()
     assert _guards_intact(kb_buf, 0x7FC0BEEF), "kbar guard band overwritten"
+    assert _guards_intact(k3_buf, 0x7FBF), "kbar3 guard band overwritten"
     assert _guards_intact(ix_buf, 0x5A5A5A5A), "block_idx guard band overwritten"
     assert _guards_intact(o_buf, 0x7FBF if dt == torch.bfloat16 else 0x7FC0BEEF), \
         "out guard band overwritten"
