@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ cu_blocks, int total_tokens, int tiles_per_seq, int nunits,
     int tile_tokens, int H, int h0, int HC, int NB, int block_size, int topk, int slot_stride,
-    int dense_blocks, int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ list) {
+    int dense_blocks, const int32_t* __restrict__ notfull, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ list) {
   __shared__ int32_t hist[kScatterBins];
   __shared__ int32_t loff[kScatterBins + 1];
   __shared__ int32_t gbase[kScatterBins];
@@ -142,11 +142,24 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
   if (nbins == 0) return;
   const int gb0 = cu_blocks[sid];
   const size_t key0 = (size_t)hl * NB + gb0;
+  // a block below dense_blocks whose notfull flag is 0 holds only
+  // dense-prefix rows: they are skipped without reading them, and a tile of
+  // such blocks has nothing to do
+  auto all_dense = [&](int cb) {
+    return cb < dense_blocks && gb0 + cb < NB && notfull[key0 + cb] == 0;
+  };
+  {
+    bool skip = true;
+    for (int cb = p0 / block_size; cb <= (p1 - 1) / block_size && skip; ++cb)
+      skip = all_dense(cb);
+    if (skip) return;
+  }
   // calls f(e, slot, p) for each accepted historical entry of row p (the
   // rule of accept_hist, inside the batch's blocks): at most topk - 1 per
   // row, so a tile stages at most tile_tokens * (topk - 1) entries
   auto walk = [&](int p, auto&& f) {
     const int c = p / block_size;
+    if (all_dense(c)) return;
     const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + hl) * topk;
     if (dense_row(row, topk, c, dense_blocks)) return;
     int last = -1, nh = 0;
@@ -317,7 +330,7 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
                        block_idx,
                        g.cu_seqlens, g.cu_blocks, g.total_tokens, stiles, nunits, rt,
                        g.num_heads, g.head_lo, g.head_cnt, g.total_blocks, g.block_size, topk,
-                       slot_stride, dense_blocks, counts, offsets, list);
+                       slot_stride, dense_blocks, notfull, counts, offsets, list);
   }
   if (tile_info && max_tiles > 0)
     hipLaunchKernelGGL(tile_info_kernel, dim3((unsigned)((max_tiles + 255) / 256)), dim3(256), 0,

@@ -126,9 +126,19 @@ __device__ __forceinline__ bool accept_hist(int e, int c, int last, int nh, int 
 }
 __device__ __forceinline__ int count_hist(const int32_t* __restrict__ row, int topk, int c) {
   int nh = 0, last = -1;
-  for (int j = 0; j < topk; ++j) {
-    int e = row[j];
+  auto visit = [&](int e) {
     if (accept_hist(e, c, last, nh, topk)) { ++nh; last = e; }
+  };
+  if ((topk & 3) == 0) {  // rows are 16-byte aligned: whole int4 loads
+    for (int j = 0; j < topk; j += 4) {
+      const int4 e4 = *reinterpret_cast<const int4*>(row + j);
+      visit(e4.x);
+      visit(e4.y);
+      visit(e4.z);
+      visit(e4.w);
+    }
+  } else {
+    for (int j = 0; j < topk; ++j) visit(row[j]);
   }
   return nh;
 }
