@@ -168,27 +168,34 @@ def test_moba_8k(dev, out_dtype):
     print("8k", out_dtype, st, st2)
 
 
-@pytest.mark.parametrize("name,per_head,heads", [
-    ("32k", 128, [0, 5, 31]),
-    ("varlen", 96, [0, 17]),
+@pytest.mark.parametrize("name,per_head,heads,sel_heads", [
+    ("32k", 512, [0, 5, 11, 19, 26, 31], []),
+    ("varlen", 512, [0, 9, 17, 30], [3, 29]),
 ])
-def test_moba_sampled(dev, name, per_head, heads):
+def test_moba_sampled(dev, name, per_head, heads, sel_heads):
+    """Outputs of seeded rows (per_head per listed head) against the oracle
+    on the selection the oracle confirms, and (sel_heads) the selections of
+    every row of further heads."""
     w = inputs.WORKLOADS[name]
     x, geom, out, lse, idx = _run(w, dev)
     rows = inputs.sample_rows(w, per_head, heads=heads)
     st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
                                 w.scale, out, lse, idx, rows, parity.BF16_TOL)
     print(name, st)
+    if sel_heads:
+        st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk,
+                                       idx, heads=sel_heads)
+        print(name, "selections of heads", sel_heads, st)
 
 
 def test_moba_1m_sampled(dev):
     """The 1M-token workload in the launch configuration bench.py times:
-    outputs on 1024 seeded rows (8 heads), selections on every row of two
+    outputs on 2048 seeded rows (8 heads), selections on every row of two
     heads, and causal validity of every selection row; then the same
     attention in passes of 8 heads, which must reproduce it bit for bit."""
     w = inputs.WORKLOADS["1m"]
     x, geom, out, lse, idx = _run(w, dev)
-    rows = inputs.sample_rows(w, 128, heads=[0, 3, 9, 14, 17, 22, 28, 31])
+    rows = inputs.sample_rows(w, 256, heads=[0, 3, 9, 14, 17, 22, 28, 31])
     st = parity.check_moba_rows(x["q"], x["k"], x["v"], x["cu_seqlens"], w.block_size, w.topk,
                                 w.scale, out, lse, idx, rows, parity.BF16_TOL)
     print("1m", st)
