@@ -48,40 +48,89 @@ def dense_pairs(seqlens, H):
     return H * sum(L * (L + 1) // 2 for L in seqlens)
 
 
+def mfma_tile_q(key_range):
+    """Query columns of a dense / own-block tile (launch.h: 8 waves of 32 for
+    key ranges of 1024 and more, else 4)."""
+    return 32 * (8 if key_range >= 1024 else 4)
+
+
+def prefix_route(seqlens, B, k, H, dtype):
+    """Whether moba_attn_fwd sends the rows of each sequence's first k blocks
+    that select every earlier block through its dense kernel (the library's
+    rule, api.cpp: bf16, and a dense launch over the first k B positions of
+    every sequence and all heads of at least 256 workgroups)."""
+    if dtype != "bf16" or not seqlens:
+        return False
+    span = min(max(seqlens), k * B)
+    if span <= 0:
+        return False
+    tq = mfma_tile_q(span)
+    return (span + tq - 1) // tq * len(seqlens) * H >= 256
+
+
+def attended_pairs_by_kernel(seqlens, B, k, H, route):
+    """(historical, own, prefix) attended pairs as the kernels split them:
+    with the dense-prefix route, rows of the first k blocks (each selects every
+    earlier block under the gates timed here) attend their t + 1 keys in the
+    dense prefix launch, not in the historical and own-block kernels."""
+    import numpy as np
+    hist = own = pre = 0
+    for L in seqlens:
+        t = np.arange(L, dtype=np.int64)
+        c = t // B
+        dense = (c < k) if route else np.zeros(L, dtype=bool)
+        pre += int((t + 1)[dense].sum())
+        own += int((t % B + 1)[~dense].sum())
+        hist += int((B * np.minimum(k - 1, c))[~dense].sum())
+    return H * hist, H * own, H * pre
+
+
 # tile policy of the library's attention grids (launch.h): resident
 # historical tiles when K and V^T of a block fit in 128 KiB of LDS, else
 # 32-query columns on 8 waves (B >= 1024) or 4; own-block tiles of 4 waves
 RESIDENT_LDS_BYTES = 128 * 1024
 
 
-def issued_pairs(list_lengths, seqlens, B, d):
+def issued_pairs(list_lengths, seqlens, B, d, k=0, route=False):
     """(query, key) pairs the attention kernels put through the MFMA units,
-    padding included: historical rows rounded up to the rows a tile computes
-    (32 per wave pass in resident tiles, whole tiles otherwise) against all B
-    keys of the block, and own-block tiles of 128 query columns against
-    64-key chunks up to their last query.  list_lengths holds the number of
-    historical selections of each (head, KV block)."""
+    padding included, per head for own and prefix: historical rows rounded up
+    to the rows a tile computes (32 per wave pass in resident tiles, whole
+    tiles otherwise) against all B keys of the block; own-block tiles of 128
+    query columns against 64-key chunks up to their last query (blocks of the
+    dense prefix skipped when route); and, when route, the dense prefix
+    launch's tiles over the first k B positions against 64-key chunks up to
+    their last query.  list_lengths holds the number of historical selections
+    of each (head, KV block), prefix rows left out when route."""
     import numpy as np
     n = np.asarray(list_lengths, dtype=np.int64)
     if B * d * 4 <= RESIDENT_LDS_BYTES:
         rows = (n + 31) // 32 * 32
     else:
-        tq = 32 * (8 if B >= 1024 else 4)
+        tq = mfma_tile_q(B)
         rows = (n + tq - 1) // tq * tq
     hist = int(rows.sum()) * B
-    own = 0
+    own = pre = 0
+    span = min(max(seqlens), k * B) if route else 0
+    tqp = mfma_tile_q(span) if route else 0
     for L in seqlens:
         for blo in range(0, L, B):
+            if route and blo // B < k:
+                continue
             blen = min(B, L - blo)
             for q_lo in range(0, blen, 128):
                 q_hi = min(q_lo + 128, blen)
                 own += 128 * 64 * ((q_hi + 63) // 64)
-    return hist, own
+        if route:
+            for q_lo in range(0, min(L, span), tqp):
+                q_hi = min(q_lo + tqp, L, span)
+                pre += tqp * 64 * ((q_hi + 63) // 64)
+    return hist, own, pre
 
 
-def list_lengths(torch, idx, seqlens, B):
+def list_lengths(torch, idx, seqlens, B, min_c=0):
     """Historical selections per (head, global KV block) of block_idx
-    [T, H, k] (entries below the query's own block)."""
+    [T, H, k] (entries below the query's own block), of the rows whose own
+    block is min_c or later."""
     T, H, _ = idx.shape
     dev = idx.device
     starts, blocks = [0], [0]
@@ -97,7 +146,7 @@ def list_lengths(torch, idx, seqlens, B):
     counts = torch.zeros(H * nb, dtype=torch.int64, device=dev)
     for h in range(H):  # one head at a time bounds the temporaries
         row = idx[:, h, :].to(torch.int64)
-        valid = (row >= 0) & (row < c[:, None])
+        valid = (row >= 0) & (row < c[:, None]) & (c[:, None] >= min_c)
         key = h * nb + cb[seq][:, None] + row
         counts += torch.bincount(key[valid], minlength=H * nb)
     return counts.cpu().numpy()
@@ -317,7 +366,9 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
         print(f"[bench] {w.name}: dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
     prof.detach()
     prof.close()
-    lengths = list_lengths(torch, idx, w.seqlens, w.block_size) if w.dtype == "bf16" else None
+    route = prefix_route(list(w.seqlens), w.block_size, w.topk, H, w.dtype)
+    lengths = (list_lengths(torch, idx, w.seqlens, w.block_size, w.topk if route else 0)
+               if w.dtype == "bf16" else None)
     del kbar, kbar3, idx, out, lse
     if not keep:
         del x, q, k, v
@@ -502,7 +553,9 @@ def main():
         torch, inputs, moba, w, dev, args.steps, args.warmup, args.dense_reps, keep=True)
     H, d = w.heads, w.head_dim
     q = x["q"]
-    pairs, hist_p, own_p = attended_pairs(w.seqlens, w.block_size, w.topk, H)
+    pairs, _, _ = attended_pairs(w.seqlens, w.block_size, w.topk, H)
+    route = prefix_route(list(w.seqlens), w.block_size, w.topk, H, w.dtype)
+    hist_p, own_p, pre_p = attended_pairs_by_kernel(w.seqlens, w.block_size, w.topk, H, route)
     flops = 4.0 * d * pairs
     eff_tflops = flops / (ms_step * 1e-3) / 1e12
     stages = {name: {"launches_per_step": n / args.steps, "ms_per_step": ms / args.steps}
@@ -519,17 +572,23 @@ def main():
                 "avg_launch_ms": avg_h, "flops_per_launch": hist_flops}
     n_o, ms_o = kern.get("attn_own", (0, 0.0))
     own_tflops = 4.0 * d * own_p / (ms_o / max(n_o, 1) * 1e-3) / 1e12 if ms_o > 0 else None
-    # both attention kernels together: 4d flops per attended pair over their summed time
-    t_attn = avg_h + (ms_o / max(n_o, 1) if ms_o > 0 else 0.0)
+    n_x, ms_x = kern.get("attn_prefix", (0, 0.0))
+    prefix_tflops = 4.0 * d * pre_p / (ms_x / max(n_x, 1) * 1e-3) / 1e12 if ms_x > 0 else None
+    # the attention kernels together (historical, own block, dense prefix):
+    # 4d flops per attended pair over their summed time
+    t_attn = (avg_h + (ms_o / max(n_o, 1) if ms_o > 0 else 0.0)
+              + (ms_x / max(n_x, 1) if ms_x > 0 else 0.0))
     attn_frac = (flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if t_attn > 0 else None
     mfma_issued = None
     if lengths is not None and t_attn > 0:
-        ih, io = issued_pairs(lengths, w.seqlens, w.block_size, d)
+        ih, io, ip = issued_pairs(lengths, w.seqlens, w.block_size, d, w.topk, route)
         io *= H
+        ip *= H
         mfma_issued = {
-            "historical_pairs": ih, "own_pairs": io, "flops": 4.0 * d * (ih + io),
-            "tflops_over_attention_time": 4.0 * d * (ih + io) / (t_attn * 1e-3) / 1e12,
-            "algorithmic_share": (hist_p + own_p) / (ih + io),
+            "historical_pairs": ih, "own_pairs": io, "prefix_pairs": ip,
+            "flops": 4.0 * d * (ih + io + ip),
+            "tflops_over_attention_time": 4.0 * d * (ih + io + ip) / (t_attn * 1e-3) / 1e12,
+            "algorithmic_share": (hist_p + own_p + pre_p) / (ih + io + ip),
         }
     n_g, ms_g = kern.get("gate_topk", (0, 0.0))
     gate_bytes = (geom.total_tokens * H * d * q.element_size() + geom.total_tokens * H * w.topk * 4
@@ -565,6 +624,9 @@ def main():
         "stages": stages,
         "dense_stages": {n: {"launches": c, "ms": t} for n, (c, t) in rec_dense_stages.items()},
         "own_block_tflops": own_tflops,
+        # rows of the first k blocks through the dense kernel (attn_prefix)
+        "dense_prefix_route": route,
+        "prefix_tflops": prefix_tflops,
         "attention_mfma_frac": attn_frac,
         "pool_gbps": pool_gbps,
         "pool_hbm_frac": pool_gbps / PEAK_HBM_GBPS if pool_gbps else None,
@@ -589,7 +651,10 @@ def main():
         if wo.head_group > 0:
             ms_s, wall_s, per_group, kern_s = measure_streamed(torch, inputs, moba, wo, dev,
                                                                head_chunk=wo.head_group // 2)
-            pairs_s, hist_s, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
+            pairs_s, _, _ = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)
+            hist_s = attended_pairs_by_kernel(
+                wo.seqlens, wo.block_size, wo.topk, wo.heads,
+                prefix_route(list(wo.seqlens), wo.block_size, wo.topk, wo.head_group, wo.dtype))[0]
             n_hs, ms_hs = kern_s.get("attn_hist", (0, 0.0))
             dense_x = (dense_ms * dense_pairs(wo.seqlens, wo.heads) / dense_pairs(w.seqlens, H)
                        if dense_ms else None)
@@ -651,7 +716,9 @@ def main():
         if big and dense_ms:
             dense_x = dense_ms * dense_pairs(wo.seqlens, wo.heads) / dense_pairs(w.seqlens, H)
         n_ho, ms_ho = kern_o.get("attn_hist", (0, 0.0))
-        hist_o = attended_pairs(wo.seqlens, wo.block_size, wo.topk, wo.heads)[1]
+        hist_o = attended_pairs_by_kernel(
+            wo.seqlens, wo.block_size, wo.topk, wo.heads,
+            prefix_route(list(wo.seqlens), wo.block_size, wo.topk, wo.heads, wo.dtype))[0]
         others[name] = {
             "config": {"workload": wname, "gate": gate,
                        "seqlens": list(wo.seqlens), "heads": wo.heads, "head_dim": wo.head_dim,

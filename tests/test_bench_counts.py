@@ -49,23 +49,64 @@ def test_dense_pairs_is_the_causal_count():
 
 def test_issued_pairs_hand_cases():
     # resident tiles (B 64, d 128): rows round up to 32 per wave pass
-    hist, own = bench.issued_pairs([33, 0, 64], [100], 64, 128)
-    assert hist == (64 + 0 + 64) * 64
+    hist, own, pre = bench.issued_pairs([33, 0, 64], [100], 64, 128)
+    assert hist == (64 + 0 + 64) * 64 and pre == 0
     # own block: blocks of 64 and 36 queries, one 128-column tile of one
     # 64-key chunk each
     assert own == 2 * 128 * 64
     # B 1024: 8-wave tiles of 256 rows; the own block of a 1500-token
     # sequence: block 0 has 8 tiles (chunks up to 2, 4, .., 16), block 1
     # (476 queries) 4 tiles (chunks 2, 4, 6, 8)
-    hist, own = bench.issued_pairs([300, 256, 1], [1500], 1024, 128)
+    hist, own, _ = bench.issued_pairs([300, 256, 1], [1500], 1024, 128)
     assert hist == (512 + 256 + 256) * 1024
     assert own == 128 * 64 * (sum(range(2, 17, 2)) + (2 + 4 + 6 + 8))
     # B 512 at d 128 is not resident: 4-wave tiles of 128 rows
-    hist, _ = bench.issued_pairs([129], [512], 512, 128)
+    hist, _, _ = bench.issued_pairs([129], [512], 512, 128)
     assert hist == 256 * 512
     # d 64 keeps B 512 resident
-    hist, _ = bench.issued_pairs([129], [512], 512, 64)
+    hist, _, _ = bench.issued_pairs([129], [512], 512, 64)
     assert hist == 160 * 512
+    # the dense-prefix route at k 2, B 64: the own block of block 0 and 1 is
+    # not issued (blocks 2..: 100 - 128 < 0, none here), the prefix launch
+    # covers the first 128 positions in 4-wave tiles of 128 columns, 64-key
+    # chunks up to the tile's last query
+    _, own, pre = bench.issued_pairs([0, 0], [100], 64, 128, k=2, route=True)
+    assert own == 0 and pre == 128 * 64 * 2
+    _, own, pre = bench.issued_pairs([0, 0, 0], [150], 64, 128, k=2, route=True)
+    assert own == 128 * 64 * 1 and pre == 128 * 64 * 2
+
+
+@pytest.mark.parametrize("seqlens,B,k,H", [
+    ([1000, 0, 129, 1, 300], 64, 4, 3),
+    ([4096 + 17], 256, 12, 2),
+    ([520, 1100], 128, 16, 2),
+])
+def test_pairs_by_kernel(seqlens, B, k, H):
+    tot, hist, own = bench.attended_pairs(seqlens, B, k, H)
+    assert bench.attended_pairs_by_kernel(seqlens, B, k, H, False) == (hist, own, 0)
+    h2, o2, p2 = bench.attended_pairs_by_kernel(seqlens, B, k, H, True)
+    assert h2 + o2 + p2 == tot
+    # the prefix rows (own block below k) attend t + 1 keys each
+    assert p2 == H * sum(min(L, k * B) * (min(L, k * B) + 1) // 2 for L in seqlens)
+
+
+def test_prefix_route_follows_the_library():
+    """bench.prefix_route mirrors moba_attn_fwd's choice (api.cpp: at least
+    kPrefixMinGrid = 256 workgroups of a dense launch over all heads)."""
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    api = open(os.path.join(root, "block_sparse_long_03_amd", "csrc", "api.cpp")).read()
+    launch = open(os.path.join(root, "block_sparse_long_03_amd", "csrc", "launch.h")).read()
+    assert re.search(r"constexpr long long kPrefixMinGrid = 256;", api)
+    assert "dense_grid(g, q_limit) >= moba::kPrefixMinGrid" in api
+    assert "* g.num_seqs * g.num_heads;" in launch
+    # 8K (16 heads, B 512, k 4): 8 tiles of 256 x 16 heads = 128 workgroups
+    assert not bench.prefix_route([8192], 512, 4, 16, "bf16")
+    # 32K (32 heads, B 256, k 32): 32 tiles x 32 heads
+    assert bench.prefix_route([32768], 256, 32, 32, "bf16")
+    assert bench.prefix_route([65536, 32768, 16384, 16384], 4096, 12, 32, "bf16")
+    assert bench.prefix_route([1 << 20], 4096, 12, 32, "bf16")
+    assert not bench.prefix_route([1 << 20], 4096, 12, 32, "f32")
 
 
 def test_list_lengths_counts_historical_selections():
@@ -94,6 +135,10 @@ def test_list_lengths_counts_historical_selections():
     assert np.array_equal(got, want)
     # every historical selection of a row lands in exactly one list
     assert got.sum() == sum(H * min(k - 1, t // B) for L in seqlens for t in range(L))
+    # rows whose own block is below min_c are left out
+    got2 = bench.list_lengths(torch, idx, seqlens, B, min_c=k)
+    assert got2.sum() == sum(H * min(k - 1, t // B) for L in seqlens for t in range(L)
+                             if t // B >= k)
 
 
 def test_issued_pairs_follows_the_launch_policy():
