@@ -71,6 +71,7 @@ struct MfmaArgs {
   int dense_blocks;    // own: blocks below it whose notfull flag is 0 are skipped
   const int32_t* notfull;
   float scale2;        // softmax scale * log2(e)
+  uint32_t topk_magic; // floor((2^32 - 1) / topk): list entries split without a division
   const int32_t* list;
   const int4* tile_info;  // hist: {key, first entry, end entry, 0} per tile, key < 0 past the end
   void* o_out;  // hist/own: fp16 partials [T, H, topk, D] (V units); dense: out [T, Hs, D]
@@ -112,7 +113,11 @@ void attn_mfma_kernel(MfmaArgs a) {
   constexpr bool RES = MODE == kModeHistRes;
   constexpr bool HIST = MODE == kModeHist || RES;
   static_assert(!RES || kWaves == 8, "resident tiles run 8 waves");
-  __shared__ __attribute__((aligned(1024))) char smem[RES ? kResidentLdsBytes : 2 * BUF];
+  // K/V: the resident block or the two chunk slots; then a 4 KiB output
+  // staging tile per wave
+  constexpr int kStageBytes = 4096;
+  constexpr int kStageOff = RES ? kResidentLdsBytes : 2 * BUF;
+  __shared__ __attribute__((aligned(1024))) char smem[kStageOff + kWaves * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -357,8 +362,8 @@ void attn_mfma_kernel(MfmaArgs a) {
       if (c + 2 < nchunks) load_k(c + 2, CS);
       if (MORE) load_v(NS);
     }
-    const uint32_t kb = opaque(kbase0 + kshift);
-    const uint32_t vb = opaque(vbase0 + vshift);
+    const uint32_t kb = opaque(kbase0) + kshift;
+    const uint32_t vb = opaque(vbase0) + vshift;
     const float base_old = m_use == -INFINITY ? 0.f : m_use;
     bf16x8 kf[KS], kg[KS];
     f16x8 vf[NPV], vg[NPV];
@@ -411,7 +416,7 @@ void attn_mfma_kernel(MfmaArgs a) {
       }
     }
     // ---- B
-    const uint32_t kb2 = opaque(kbase0 + kshift);
+    const uint32_t kb2 = opaque(kbase0) + kshift;
     f16x8 P0[2], P1[2];
     if (MORE) {
 #pragma unroll
@@ -445,6 +450,43 @@ void attn_mfma_kernel(MfmaArgs a) {
     }
     fence();
   };
+  // Output rows (fp16 partials, or bf16 dense output) leave through the
+  // wave's LDS staging tile, 64 dims at a time, so that eight lanes store one
+  // whole 128-byte line of a row: the accumulator layout gives a lane only
+  // 8 bytes of each of its row's lines, and a row would otherwise cost
+  // sixteen 16-byte pieces instead of two line writes.  dst[i] is row
+  // (lane >> 3) + 8 i of the wave's 32 query columns, already offset by this
+  // lane's 16-byte segment (lane & 7); CHECKED: null for rows not stored.
+  auto stage_out = [&](float inv, char* const* dst, auto checked_t) {
+    constexpr bool CHECKED = decltype(checked_t)::value;
+    const int ln = (int)opaque((uint32_t)lane);
+    const int row = ln & 31, half = ln >> 5;
+    char* stg = smem + kStageOff + w * kStageBytes;
+#pragma unroll
+    for (int dp = 0; dp < DT / 2; ++dp) {
+#pragma unroll
+      for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& Od = O[2 * dp + dl];
+          const float x0 = Od[4 * g] * inv, x1 = Od[4 * g + 1] * inv;
+          const float x2 = Od[4 * g + 2] * inv, x3 = Od[4 * g + 3] * inv;
+          u32x2 v2;
+          if (MODE == kModeDense) v2 = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          else v2 = u32x2{pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
+          *reinterpret_cast<u32x2*>(stg + row * 128 + (((dl * 4 + g) ^ (row & 7)) << 4) +
+                                    8 * half) = v2;
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (ln >> 3) + 8 * i;
+        const u32x4 d4 =
+            *reinterpret_cast<const u32x4*>(stg + r * 128 + (((ln & 7) ^ (r & 7)) << 4));
+        if (!CHECKED || dst[i] != nullptr)
+          *reinterpret_cast<u32x4*>(dst[i] + dp * 128) = d4;
+      }
+    }
+  };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
   if constexpr (!RES) {
@@ -472,14 +514,31 @@ void attn_mfma_kernel(MfmaArgs a) {
     }
 
     // ---------------- epilogue ----------------
-    if (qtok < 0) return;  // both lanes of a query column take the same branch
     float out_scale = 1.f;
     if (MODE == kModeDense) out_scale = __builtin_ldexpf(1.0f, v_exponent(a.vmax_bits[h]));
     const float l_tot = sum_with_partner(l_run);
     const float inv = out_scale / l_tot;
     const float lse_val = (m_use + log2f(l_tot)) * kLn2;
     // O[dt][r] is output dim 32 dt + 8 (r / 4) + 4 hf + (r % 4)
-    if (MODE == kModeDense && !OUT_BF16) {
+    if (MODE != kModeDense || OUT_BF16) {
+      // 2-byte rows go out through the staging tile; every lane takes part
+      // (columns without a query stage values that are never stored)
+      char* dst[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (lane >> 3) + 8 * i;
+        const int lo = __shfl((int)(uint32_t)oidx, r);
+        const int hi = __shfl((int)(oidx >> 32), r);
+        const long long orow = ((long long)hi << 32) | (uint32_t)lo;
+        dst[i] = __shfl(qtok, r) >= 0 ? (char*)a.o_out + orow * (D * 2) + (lane & 7) * 16
+                                      : nullptr;
+      }
+      stage_out(inv, dst, yes());
+      if (qtok >= 0 && hf == 0) a.lse_out[oidx] = lse_val;
+      return;
+    }
+    if (qtok < 0) return;  // both lanes of a query column take the same branch
+    {
       float* op = (float*)a.o_out + (size_t)oidx * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -489,57 +548,59 @@ void attn_mfma_kernel(MfmaArgs a) {
                       O[dt][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * g + 4 * hf) = v4;
         }
-    } else {
-      uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
-          const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
-          u32x2 v2;
-          if (MODE == kModeDense) v2 = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-          else v2 = u32x2{pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
-          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
-        }
     }
     if (hf == 0) a.lse_out[oidx] = lse_val;
   } else {
     // ---------------- resident passes ----------------
     // the whole block once, chunk ch in slot ch; LDS is read-only afterwards,
-    // so each wave runs its passes of 32 gathered queries without barriers
+    // so each wave runs its passes of 32 gathered queries without barriers.
+    // A pass's list entries are read one pass ahead, and its queries are
+    // gathered right after the previous pass's last QK^T (the query registers
+    // are free from there), ahead of that pass's output stores, so the gather
+    // overlaps the last chunk and the epilogue and does not queue behind the
+    // stores.  Lanes past the tile's end take the entry of the pass's first
+    // row: they compute that query again, bit for bit, and store the same
+    // values to the same place, so no store or load needs a branch.
+    auto entry = [&](int r, int ln32) {
+      const int j = r + ln32 < ti.z ? r + ln32 : min(r, ti.z - 1);
+      return a.list[j];
+    };
+    auto gather = [&](int ent) {
+      const int tok = (int)__umulhi((uint32_t)ent, a.topk_magic);  // ent / topk, or one less
+      const int tq = ent - tok * a.topk >= a.topk ? tok + 1 : tok;
+      const int ln = (int)opaque((uint32_t)lane);
+      const uint16_t* qp = a.q + ((size_t)tq * a.Hs + hg) * D + 8 * (ln >> 5);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+    };
     for (int ch = 0; ch < nchunks; ++ch) {
       load_k(ch, ch);
       load_v(ch);
     }
+    int r0 = ti.y + w * 32;
+    int ent = entry(r0, l32);
+    gather(ent);
+    // the first pass's queries have landed before the loop: inside it, the
+    // query registers then only ever wait for the gather issued one pass
+    // earlier, never for the output stores queued behind it
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qreg[ks]));
     __syncthreads();
     f32x16 S0, S1, N0, N1;
-    for (int r0 = ti.y + w * 32; r0 < ti.z; r0 += kWaves * 32) {
-      const int j = r0 + l32;
-      qtok = -1;
-      if (j < ti.z) {
-        const int ent = a.list[j];
-        qtok = ent / a.topk;
-        oidx = ((long long)qtok * a.H + h) * a.topk + (ent - qtok * a.topk);
-      }
-      {
-        const bool qv = qtok >= 0;
-        const uint16_t* qp = a.q + ((size_t)(qv ? qtok : 0) * a.Hs + hg) * D + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 wv = {0u, 0u, 0u, 0u};
-          if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-          qreg[ks] = __builtin_bit_cast(bf16x8, wv);
-        }
-      }
+    for (; r0 < ti.z; r0 += kWaves * 32) {
+      const int ent_next = entry(r0 + kWaves * 32, (int)opaque((uint32_t)lane) & 31);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
       m_use = -INFINITY;
       l_run = 0.f;
-      S0 = qk(kbase0, 0, 0);
-      S1 = qk(kbase0, 0, 1);
+      {
+        const uint32_t kb0 = opaque(kbase0);
+        S0 = qk(kb0, 0, 0);
+        S1 = qk(kb0, 0, 1);
+      }
       int c = 0;
       for (; c + 2 < nchunks; c += 2) {
         iteration(c, S0, S1, N0, N1, no(), yes());
@@ -551,22 +612,27 @@ void attn_mfma_kernel(MfmaArgs a) {
       } else {
         iteration(c, S0, S1, N0, N1, no(), no());
       }
+      gather(ent_next);
       // fp16 partial (V units) and lse of the pass's rows
-      if (qtok >= 0) {
+      {
+        auto out_row = [&](int e) {  // partial row of list entry e
+          int qt = (int)__umulhi((uint32_t)e, a.topk_magic);  // e / topk, or one less
+          int slot = e - qt * a.topk;
+          if (slot >= a.topk) { ++qt; slot -= a.topk; }
+          return ((long long)qt * a.H + h) * a.topk + slot;
+        };
         const float l_tot = sum_with_partner(l_run);
-        const float inv = 1.f / l_tot;
-        uint16_t* op = (uint16_t*)a.o_out + (size_t)oidx * D;
+        const int ln = (int)opaque((uint32_t)lane);
+        a.lse_out[out_row(ent)] = (m_use + log2f(l_tot)) * kLn2;  // both lanes: same value
+        char* dst[4];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float x0 = O[dt][4 * g] * inv, x1 = O[dt][4 * g + 1] * inv;
-            const float x2 = O[dt][4 * g + 2] * inv, x3 = O[dt][4 * g + 3] * inv;
-            const u32x2 v2 = {pack_f16x2(x0, x1), pack_f16x2(x2, x3)};
-            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hf) = v2;
-          }
-        if (hf == 0) a.lse_out[oidx] = (m_use + log2f(l_tot)) * kLn2;
+        for (int i = 0; i < 4; ++i) {
+          const int e = __shfl(ent, (ln >> 3) + 8 * i);
+          dst[i] = (char*)a.o_out + (size_t)out_row(e) * (D * 2) + (ln & 7) * 16;
+        }
+        stage_out(1.f / l_tot, dst, no());
       }
+      ent = ent_next;
     }
   }
 }
@@ -588,6 +654,7 @@ static MfmaArgs base_args(const void* q, const void* k, const uint16_t* vt, cons
   a.topk = topk;
   a.NB = g.total_blocks;
   a.scale2 = scale * kLog2e;
+  a.topk_magic = 0xFFFFFFFFu / (uint32_t)topk;
   a.q_limit = 0x7fffffff;
   return a;
 }
