@@ -54,10 +54,11 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t unit, void*
   __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (lds_dma_t*)dst, 16, unit, 0, 0, 0, 0);
 }
 
-// fp16 <-> fp32 (round to nearest even).
+// fp16 <-> fp32 (round to nearest even); the pair in one packed conversion.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
 }
 __device__ __forceinline__ float lo_f16(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
