@@ -467,6 +467,9 @@ void attn_mfma_kernel(MfmaArgs a) {
   // sixteen 16-byte pieces instead of two line writes.  dst[i] is row
   // (lane >> 3) + 8 i of the wave's 32 query columns, already offset by this
   // lane's 16-byte segment (lane & 7); CHECKED: null for rows not stored.
+  // The stores are non-temporal: the rows are read once, by a later kernel,
+  // and keep the L2 for the K/V chunks (32K: historical 4.15 -> 4.05 ms,
+  // own block 0.254 -> 0.215 ms).
   auto stage_out = [&](float inv, char* const* dst, auto checked_t) {
     constexpr bool CHECKED = decltype(checked_t)::value;
     const int ln = (int)opaque((uint32_t)lane);
@@ -493,7 +496,7 @@ void attn_mfma_kernel(MfmaArgs a) {
         const u32x4 d4 =
             *reinterpret_cast<const u32x4*>(stg + r * 128 + (((ln & 7) ^ (r & 7)) << 4));
         if (!CHECKED || dst[i] != nullptr)
-          *reinterpret_cast<u32x4*>(dst[i] + dp * 128) = d4;
+          __builtin_nontemporal_store(d4, reinterpret_cast<u32x4*>(dst[i] + dp * 128));
       }
     }
   };
