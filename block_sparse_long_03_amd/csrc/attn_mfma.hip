@@ -666,12 +666,15 @@ void attn_mfma_kernel(MfmaArgs a) {
         };
         const float l_tot = sum_with_partner(l_run);
         const int ln = (int)opaque((uint32_t)lane);
-        a.lse_out[out_row(ent)] = (m_use + log2f(l_tot)) * kLn2;  // both lanes: same value
+        const long long orow = out_row(ent);
+        a.lse_out[orow] = (m_use + log2f(l_tot)) * kLn2;  // both lanes: same value
         char* dst[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = __shfl(ent, (ln >> 3) + 8 * i);
-          dst[i] = (char*)a.o_out + (size_t)out_row(e) * (D * 2) + (ln & 7) * 16;
+          const int r = (ln >> 3) + 8 * i;
+          const int lo = __shfl((int)(uint32_t)orow, r);
+          const int hi = __shfl((int)(orow >> 32), r);
+          dst[i] = (char*)a.o_out + (((long long)hi << 32) | (uint32_t)lo) * (D * 2) + (ln & 7) * 16;
         }
         stage_out(1.f / l_tot, dst, no());
       }

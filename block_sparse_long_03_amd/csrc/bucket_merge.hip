@@ -352,13 +352,15 @@ hipError_t launch_bucket(const int32_t* block_idx, const Geo& g, int topk, int t
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v,
                                                    int total_tokens, int hd, int head_dim,
-                                                   int h0, uint32_t* __restrict__ vmax_bits) {
+                                                   int h0, int span,
+                                                   uint32_t* __restrict__ vmax_bits) {
   __shared__ uint32_t red[256];
   const int col0 = h0 * head_dim + blockIdx.y * 64;  // 64 columns of one head
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
-  const int t0 = blockIdx.x * 2048;
+  const long long t0 = (long long)blockIdx.x * span;  // span tokens per workgroup
   uint32_t m = 0u;
-  for (int t = t0 + ty; t < min(total_tokens, t0 + 2048); t += 32) {
+  const int t_end = (int)min((long long)total_tokens, t0 + span);
+  for (int t = (int)t0 + ty; t < t_end; t += 32) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(v + (size_t)t * hd + col0 + tx * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -432,10 +434,14 @@ hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, 
   const int hd = g.num_heads * g.head_dim;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, st, (int32_t*)vmax_bits,
                      g.head_cnt);
-  hipLaunchKernelGGL(vmax_kernel,
-                     dim3((g.total_tokens + 2047) / 2048, g.head_cnt * g.head_dim / 64),
-                     dim3(256), 0, st, (const uint16_t*)v, g.total_tokens, hd, g.head_dim,
-                     g.head_lo, vmax_bits);
+  // 2048 tokens per workgroup, fewer (down to 256) while that leaves the
+  // grid under 2048 workgroups
+  const int cols = g.head_cnt * g.head_dim / 64;
+  int span = 2048;
+  while (span > 256 && (long long)((g.total_tokens + span - 1) / span) * cols < 2048) span /= 2;
+  hipLaunchKernelGGL(vmax_kernel, dim3((g.total_tokens + span - 1) / span, cols), dim3(256), 0,
+                     st, (const uint16_t*)v, g.total_tokens, hd, g.head_dim, g.head_lo, span,
+                     vmax_bits);
   dim3 grid(g.total_blocks * (g.block_size / 64), g.head_cnt);
   if (g.head_dim == 128)
     hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)v,
