@@ -320,10 +320,10 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    prof = moba.Profiler().attach()
-    prof.reset()
-    # one event pair per step on the stream the library launches on, for the
-    # median and minimum next to the mean of the wall clock
+    # The timed region runs with no per-launch profiler attached: its two
+    # events per kernel cost a few microseconds each, which is 15% of an 8K
+    # step.  One event pair per step on the stream the library launches on
+    # gives the median and minimum next to the mean of the wall clock.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
@@ -338,6 +338,13 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
     per_step = sorted(a.elapsed_time(b) for a, b in ev)
     step_stats = {"mean_ms": ms_step, "median_ms": per_step[len(per_step) // 2],
                   "min_ms": per_step[0], "max_ms": per_step[-1]}
+    # per-kernel times: the same number of steps again, each launch
+    # bracketed by HIP events on its stream
+    prof = moba.Profiler().attach()
+    prof.reset()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     kern = prof.summary()
     prof.reset()
     print(f"[bench] {w.name}: moba {ms_step:.3f} ms/step (median {step_stats['median_ms']:.3f},"
@@ -355,12 +362,16 @@ def measure(torch, inputs, moba, w, dev, steps, warmup, dense_reps, keep=False, 
         dlse = torch.empty_like(lse)
         moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
         torch.cuda.synchronize()
-        prof.reset()
+        prof.detach()  # timed like the MoBA steps, then once more for its stages
         t0 = time.perf_counter()
         for _ in range(dense_reps):
             moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
         torch.cuda.synchronize()
         dense_ms = (time.perf_counter() - t0) * 1e3 / dense_reps
+        prof.attach()
+        prof.reset()
+        moba.moba_dense_causal_fwd(q, k, v, geom, w.scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
         rec_dense_stages = prof.summary()
         del dout, dws
         print(f"[bench] {w.name}: dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
