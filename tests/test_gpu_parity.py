@@ -425,6 +425,9 @@ def test_k_ge_n_matches_own_dense_kernel(dev):
 
 @pytest.mark.parametrize("w", [
     inputs.custom([1000, 0, 64, 2000], 2, 128, 128, 2, "bf16", name="dense-varlen"),
+    # 8-wave tiles (a 2000-token sequence in the batch) over sequences of 1,
+    # 2 and 3 key chunks: the four-slot ring's short tails
+    inputs.custom([2000, 100, 150, 40], 2, 128, 128, 2, "bf16", name="dense-ring-tails"),
     inputs.custom([900, 35], 2, 64, 64, 2, "bf16", name="dense-d64"),
     inputs.custom([1500, 35], 2, 64, 64, 2, "bf16", name="dense-d64-long"),
     inputs.custom([300, 129], 2, 128, 64, 2, "f32", name="dense-f32"),
