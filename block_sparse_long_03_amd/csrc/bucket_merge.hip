@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
     const int c = (t - cu_seqlens[s]) / block_size;
     const int nh = count_hist(block_idx + grow * topk, topk, c);
     dense = c < dense_blocks && nh == c;
-    nparts = nh + 1;
+    nparts = dense ? 0 : nh + 1;  // dense-prefix rows: no partials to weigh
     // part i < nh lives in slot i; the own block in slot topk - 1
     float l4[4];
     float mx = -INFINITY;
