@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -156,11 +157,19 @@ def list_lengths(torch, idx, seqlens, B, min_c=0):
 HIST_SOURCES = ("attn_mfma.hip", "common.h", "launch.h")
 
 
+def code_tokens(text):
+    """C++ source without comments and with whitespace runs collapsed: a
+    change to a comment leaves the code, and with it a counter record, valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(*names):
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "block_sparse_long_03_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_long_03_amd", "csrc", n)) as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

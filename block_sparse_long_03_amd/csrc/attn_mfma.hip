@@ -598,12 +598,13 @@ void attn_mfma_kernel(MfmaArgs a) {
     // the whole block once, chunk ch in slot ch; LDS is read-only afterwards,
     // so each wave runs its passes of 32 gathered queries without barriers.
     // A pass's list entries are read one pass ahead, and its queries are
-    // gathered right after the previous pass's last QK^T (the query registers
-    // are free from there), ahead of that pass's output stores, so the gather
-    // overlaps the last chunk and the epilogue and does not queue behind the
-    // stores.  Lanes past the tile's end take the entry of the pass's first
-    // row: they compute that query again, bit for bit, and store the same
-    // values to the same place, so no store or load needs a branch.
+    // gathered at the end of the previous pass, ahead of that pass's output
+    // stores (the vector-memory counter is in order), so the gather overlaps
+    // the epilogue and does not wait for the stores to be acknowledged; the
+    // query registers are free there.  Lanes past the tile's end take the
+    // entry of the pass's first row: they compute that query again, bit for
+    // bit, and store the same values to the same place, so no store or load
+    // needs a branch.
     auto entry = [&](int r, int ln32) {
       const int j = r + ln32 < ti.z ? r + ln32 : min(r, ti.z - 1);
       return a.list[j];
