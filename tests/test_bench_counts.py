@@ -151,3 +151,11 @@ def test_issued_pairs_follows_the_launch_policy():
     assert m and int(m.group(1)) * int(m.group(2)) == bench.RESIDENT_LDS_BYTES
     assert re.search(r"return key_range >= 1024 \? 8 : 4;", src)
     assert re.search(r"return \(long long\)block_size \* head_dim \* 4 <= kResidentLdsBytes;", src)
+
+
+def test_code_tokens_ignores_comments_only():
+    """The traffic record stays valid across comment edits, not code edits."""
+    a = "int x = 1;  // one\n/* block\n comment */ float y;\n"
+    b = "int x = 1;\nfloat   y;  // another note\n"
+    assert bench.code_tokens(a) == bench.code_tokens(b) == "int x = 1; float y;"
+    assert bench.code_tokens("int x = 2;") != bench.code_tokens(a)
