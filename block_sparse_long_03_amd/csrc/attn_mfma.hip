@@ -229,11 +229,29 @@ void attn_mfma_kernel(MfmaArgs a) {
   const int vrow0 = (w * 1024 + lane * 16) / VRB;
   const uint32_t voff0 = (uint32_t)(vrow0 * a.block_size * 2 +
                                     ((((lane * 16) % VRB) >> 4) ^ swz<VRB>(vrow0)) * 16);
+  // One buffer descriptor for the tile's keys, built once: a whole chunk's
+  // rows are then reached through the lane's record index (16-byte records,
+  // krec of them per key row), with no per-chunk address arithmetic in
+  // scalar registers.  Tiles whose key span would take the index past 2^31
+  // rebuild the descriptor per chunk instead.
+  const uint32_t krec = (uint32_t)(krow_bytes >> 4);
+  const bool kfix = (long long)(key_hi - key_lo + 2 * kTK) * krec < (1LL << 31);
+  const __amdgpu_buffer_rsrc_t rk = dma_rsrc(kseq + (size_t)key_lo * krow_bytes);
   // K rows of chunk ch into slot buf; rows past the sequence end repeat its
   // last key (they are always masked)
   auto load_k = [&](int ch, int buf) {
     const int kp0 = key_lo + ch * kTK;
     char* kl = smem + buf * BUF;
+    if (kp0 + kTK <= seq_len && kfix) {
+      const uint32_t u0 = (uint32_t)(ch * kTK) * krec + (koff0 >> 4);
+#pragma unroll
+      for (int i = 0; i < KIW; ++i) {
+        const int j = w + kWaves * i;
+        if (NKI % kWaves == 0 || j < NKI)
+          lds_dma16(rk, u0 + (uint32_t)(i * KROWS_I) * krec, kl + j * 1024);
+      }
+      return;
+    }
     const char* kb = kseq + (size_t)kp0 * krow_bytes;
     if (kp0 + kTK <= seq_len) {
 #pragma unroll
@@ -257,10 +275,27 @@ void attn_mfma_kernel(MfmaArgs a) {
   // key offset off_next inside it)
   int gb_next = gb_base + key_lo / a.block_size;
   int off_next = key_lo % a.block_size;
+  // Historical and own-block tiles read V^T of one block: one descriptor
+  // at the tile's first key, chunk c at record offset 8 c (64 keys of 2
+  // bytes); dense tiles cross blocks and address each chunk's block.
+  const __amdgpu_buffer_rsrc_t rv = dma_rsrc(
+      a.vt + ((size_t)min(gb_next, a.NB - 1) * a.H + h) * D * (size_t)a.block_size + off_next);
+  const uint32_t vrow_rec = (uint32_t)(VROWS_I * a.block_size / 8);  // records per instruction step
+  uint32_t vch = 0;  // chunks loaded so far
   auto load_v = [&](int buf) {
+    char* vl = smem + buf * BUF + KBYTES;
+    if (MODE != kModeDense) {
+      const uint32_t u0 = vch * (kTK * 2 / 16) + (voff0 >> 4);
+#pragma unroll
+      for (int i = 0; i < VIW; ++i) {
+        const int j = w + kWaves * i;
+        if (NVI % kWaves == 0 || j < NVI) lds_dma16(rv, u0 + (uint32_t)i * vrow_rec, vl + j * 1024);
+      }
+      ++vch;
+      return;
+    }
     const int gb = min(gb_next, a.NB - 1);
     const char* vb = (const char*)(a.vt + ((size_t)gb * a.H + h) * D * (size_t)a.block_size + off_next);
-    char* vl = smem + buf * BUF + KBYTES;
 #pragma unroll
     for (int i = 0; i < VIW; ++i) {
       const int j = w + kWaves * i;

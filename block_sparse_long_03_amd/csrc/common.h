@@ -48,10 +48,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // operand prefetch of the MFMA loops.
 constexpr int kBufferWord3 = 0x00020000;  // 32-bit raw data format, gfx9 family
 typedef __attribute__((address_space(3))) void lds_dma_t;
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t unit, void* dst) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 16, -1, kBufferWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 16, -1, kBufferWord3);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t unit, void* dst) {
   __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (lds_dma_t*)dst, 16, unit, 0, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t unit, void* dst) {
+  lds_dma16(dma_rsrc(base), unit, dst);
 }
 
 // fp16 <-> fp32 (round to nearest even); the pair in one packed conversion.
