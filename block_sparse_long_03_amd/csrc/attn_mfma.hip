@@ -403,9 +403,6 @@ void attn_mfma_kernel(MfmaArgs a) {
     if (RING4) {
       if (c + 3 < nchunks) load_k(c + 3, (c + 3) & 3);
       if (c + 2 < nchunks) load_v((c + 2) & 3);
-    } else if (!RES) {
-      if (c + 2 < nchunks) load_k(c + 2, CS);
-      if (MORE) load_v(NS);
     }
     const uint32_t kb = opaque(kbase0) + kshift;
     const uint32_t vb = opaque(vbase0) + vshift;
@@ -459,6 +456,13 @@ void attn_mfma_kernel(MfmaArgs a) {
         S0[r] -= delta;
         S1[r] -= delta;
       }
+    }
+    // the next chunks' loads go out after the A part, not at the iteration
+    // start where every wave of the workgroup issues its operand reads at
+    // once after the barrier (1M historical kernel 2% faster, bit-identical)
+    if (!RES && !RING4) {
+      if (c + 2 < nchunks) load_k(c + 2, CS);
+      if (MORE) load_v(NS);
     }
     // ---- B
     const uint32_t kb2 = opaque(kbase0) + kshift;
