@@ -16,7 +16,8 @@
 //              attends them: the block's historical list (queries that
 //              selected it), then the own-block queries at or after its
 //              first key (causal mask).  dK and dV stay in registers for the
-//              whole stream and are written once: no atomics, deterministic.
+//              whole stream and are written once: no atomics (the sums
+//              follow the list order, which depends on scheduling).
 //   bwd_q:     the forward's tiles (a (head, block) list tile of gathered
 //              queries, or an own-block query tile) against the block's keys
 //              in 64-key chunks; each wave keeps its 32 queries' dQ in

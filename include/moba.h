@@ -302,9 +302,10 @@ moba_status moba_attn_fwd_static(const void* q, const void* k, const void* v, in
  *   dq, dk, dv   [total_tokens, num_heads, head_dim] fp32, written in full
  *   workspace    at least moba_attn_bwd_workspace_bytes(...) bytes, 256-byte
  *                aligned; contents on entry ignored
- * dk and dv are deterministic; dq is summed with fp32 atomics over the
- * query's (at most topk) selected blocks, so its last bits may vary between
- * runs.
+ * dk and dv take no atomics, but each key's sums run over its block's query
+ * list, whose order depends on scheduling; dq is summed with fp32 atomics
+ * over the query's (at most topk) selected blocks.  The last bits of all
+ * three may therefore vary between runs (the forward's do not).
  */
 size_t moba_attn_bwd_workspace_bytes(int dtype, int total_tokens, int total_blocks,
                                      int num_heads, int head_dim, int block_size, int topk);
