@@ -664,10 +664,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_kernel(BwdArgs a) {
   }
   auto chunk = [&](int ch, auto buf_t) {
     constexpr int BF = decltype(buf_t)::value;
-    if (ch + 1 < nchunks) load_chunk(ch + 1, BF ^ 1);
     const int kp0 = key_lo + ch * kBwdChunk;
 #pragma unroll
     for (int sc = 0; sc < 2; ++sc) {
+      // the next chunk's loads go out after the first half's products, not
+      // right after the barrier where every wave reads its first operands
+      if (sc == 1 && ch + 1 < nchunks) load_chunk(ch + 1, BF ^ 1);
       const int ko = BF * BUF + sc * 32 * ROWB;  // compile-time after unrolling
       f32x16 S, dP;
 #pragma unroll
