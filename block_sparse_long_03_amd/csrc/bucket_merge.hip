@@ -195,8 +195,48 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
   }
   for (int b = threadIdx.x; b < nbins; b += kScatterThreads) hist[b] = 0;
   __syncthreads();
-  for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
-    walk(p, [&](int e, int, int) { atomicAdd(&hist[e], 1); });
+  // k <= kCacheK: the thread's one row (tiles hold at most kScatterThreads
+  // tokens) is read once, its entries kept in registers with the mask of
+  // accepted ones for the staging pass
+  constexpr int kCacheK = 16;
+  const bool cached = topk <= kCacheK;
+  const int p_me = p0 + (int)threadIdx.x;
+  int ev[kCacheK];
+  uint32_t accm = 0u;
+  if (cached) {
+    if (p_me < p1) {
+      const int c = p_me / block_size;
+      if (!all_dense(c)) {
+        const int32_t* row = block_idx + ((size_t)(start + p_me) * H + h0 + hl) * topk;
+        if ((topk & 3) == 0) {
+#pragma unroll
+          for (int q = 0; q < kCacheK; q += 4) {
+            int4 e4 = {-1, -1, -1, -1};
+            if (q < topk) e4 = *reinterpret_cast<const int4*>(row + q);
+            ev[q] = e4.x; ev[q + 1] = e4.y; ev[q + 2] = e4.z; ev[q + 3] = e4.w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < kCacheK; ++q) ev[q] = q < topk ? row[q] : -1;
+        }
+        int last = -1, nh = 0;
+#pragma unroll
+        for (int q = 0; q < kCacheK; ++q)
+          if (q < topk && accept_hist(ev[q], c, last, nh, topk)) {
+            accm |= 1u << q;
+            last = ev[q];
+            ++nh;
+          }
+        if (c < dense_blocks && nh == c) accm = 0u;  // a dense-prefix row
+#pragma unroll
+        for (int q = 0; q < kCacheK; ++q)
+          if (((accm >> q) & 1u) && gb0 + ev[q] < NB) atomicAdd(&hist[ev[q]], 1);
+      }
+    }
+  } else {
+    for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
+      walk(p, [&](int e, int, int) { atomicAdd(&hist[e], 1); });
+  }
   __syncthreads();
   // exclusive scan of the histogram (one wave), global range per block
   if (threadIdx.x < 64) {
@@ -223,10 +263,18 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     hist[b] = 0;
   }
   __syncthreads();
-  for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
-    walk(p, [&](int e, int slot, int pp) {
-      stage[loff[e] + atomicAdd(&hist[e], 1)] = value(slot, pp);
-    });
+  if (cached) {
+#pragma unroll
+    for (int q = 0; q < kCacheK; ++q)
+      if (((accm >> q) & 1u) && gb0 + ev[q] < NB)
+        stage[loff[ev[q]] + atomicAdd(&hist[ev[q]], 1)] =
+            value(__popc(accm & ((1u << q) - 1u)), p_me);
+  } else {
+    for (int p = p0 + (int)threadIdx.x; p < p1; p += kScatterThreads)
+      walk(p, [&](int e, int slot, int pp) {
+        stage[loff[e] + atomicAdd(&hist[e], 1)] = value(slot, pp);
+      });
+  }
   __syncthreads();
   // each wave copies whole runs: lanes write consecutive list entries
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
