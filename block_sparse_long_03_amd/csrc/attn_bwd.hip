@@ -495,10 +495,12 @@ __global__ __launch_bounds__(64 * kBwdPairWaves) void bwd_kv_pair_kernel(BwdArgs
   // tile t in slot SLOT = t % 3: its two halves, then the barrier
   auto tile = [&](int t, auto slot_t) {
     constexpr int SLOT = decltype(slot_t)::value;
-    // every wave is past tile t - 1: its slot takes tile t + 2
+    step(t, slot_t, c0());
+    // every wave is past tile t - 1: its slot takes tile t + 2.  The loads
+    // go out after the first half, not right after the barrier where every
+    // wave reads its first operands
     if (t + 2 < ntiles) issue_tile(t + 2, std::integral_constant<int, (SLOT + 2) % NBUF>());
     if (w == 1 && t + 4 < n_hist) issue_list(t + 4);
-    step(t, slot_t, c0());
     step(t, slot_t, c1());
     // everything issued before this iteration has landed (tile t + 1, the
     // list slice of tile t + 3); this iteration's loads stay in flight
