@@ -224,7 +224,8 @@ constexpr int kGateChunk = 128;  // past blocks per MFMA scoring step (one 32 x 
 constexpr int kGateChunkValu = 64;  // past blocks per fp32 scoring step
 constexpr int kGateWaves = 4;
 constexpr int kGateRowsPerWave = kGateRows / kGateWaves;
-// the single-span kernel: 64 query tokens and 8 waves per workgroup; the two
+// the single-span kernel: 64 query tokens and 8 waves per workgroup.  Mean
+// gate: wave w scores block tile w for all 64 tokens.  Min/max gate: the two
 // waves of a block tile (one per 32 tokens) read the same pooled-key lines
 // together, so the second read is served by the CU's L1
 constexpr int kSpanWaves = 8;
@@ -367,6 +368,73 @@ __device__ __forceinline__ void gate_scores_planes(const bf16x8 (&qfrag)[D / 16]
   for (int r = 0; r < 16; ++r) {
     const int jb = 32 * bt + 8 * (r >> 2) + 4 * hf + (r & 3);  // block in the chunk
     ss[32 * (w >> 2) + l32][gate_col(col0 + jb)] = jb < nb ? acc[r] : -INFINITY;
+  }
+}
+
+// The single-span kernel's scores (at most 256 past blocks, so at most one
+// 32-block tile per wave): wave w owns blocks 32 w .. 32 w + 31 for all 64
+// query tokens of the workgroup, with one accumulator per 32 tokens, so each
+// fragment of the pooled-key terms is fetched once per workgroup and only the
+// tiles below the row's span are computed.  Per k-step the wave loads the
+// three term fragments and the Q fragments of both token halves and issues six
+// products; each token's score is summed in the same order as in
+// gate_scores_planes (k-steps, then hi, mid, lo), so the scores are the same
+// bits.  Q rows past the sequence end load as zeros.
+template <int D>
+__device__ __forceinline__ void gate_scores_span(const uint16_t* __restrict__ q, int start, int len,
+                                                 int p0, int H, int h,
+                                                 const uint16_t* __restrict__ kbar3, int gblk0,
+                                                 int nb, int total_blocks,
+                                                 float (*ss)[kGateStride], int w, int lane) {
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int j = 32 * w + l32;  // block of this lane's A rows
+  const bool ok = j < nb && gblk0 + j < total_blocks;
+  const size_t plane = (size_t)(D / 16) * total_blocks * 16;
+  const uint16_t* kp = kbar3 + (size_t)h * 3 * plane + (size_t)(ok ? gblk0 + j : gblk0) * 16 + 8 * hf;
+  const uint16_t* qp[2];
+  bool qv[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tok = p0 + 32 * t + l32;
+    qv[t] = tok < len;
+    qp[t] = q + ((size_t)(start + (qv[t] ? tok : p0)) * H + h) * D + 8 * hf;
+  }
+  f32x16 acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  constexpr int KH = D / 32;  // k-steps per group of loads in flight together
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int half = 0; half < D / (16 * KH); ++half) {
+    u32x4 a[3][KH], b[2][KH];
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+        a[pl][kk] = *reinterpret_cast<const u32x4*>(
+            kp + pl * plane + (size_t)(half * KH + kk) * total_blocks * 16);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        b[t][kk] = qv[t] ? *reinterpret_cast<const u32x4*>(qp[t] + 16 * (half * KH + kk)) : zero;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk)
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, ok ? a[pl][kk] : zero),
+              __builtin_bit_cast(bf16x8, b[t][kk]), acc[t], 0, 0, 0);
+  }
+  // acc[t][r] = score of block 32 w + 8 (r / 4) + 4 hf + (r % 4) for token 32 t + lane & 31
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int jb = 32 * w + 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ss[32 * t + l32][gate_col(jb)] = jb < nb ? acc[t][r] : -INFINITY;
   }
 }
 
@@ -709,7 +777,13 @@ __global__ __launch_bounds__(kSpanWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     return;
   }
-  if constexpr (kMfma) {
+  if constexpr (kMfma && !QUEST) {
+    static_assert(32 * kSpanWaves == kGateSpan, "one 32-block tile per wave covers the span");
+    if (32 * w < c)
+      gate_scores_span<D>((const uint16_t*)q, start, len, p0, H, h, kbar3, gb0, c, total_blocks,
+                          ss, w, lane);
+    __syncthreads();
+  } else if constexpr (kMfma) {
     bf16x8 qfrag[D / 16];
     const int tok = p0 + 32 * (w >> 2) + (lane & 31);
     const bool qv = tok < len;
@@ -722,12 +796,8 @@ __global__ __launch_bounds__(kSpanWaves * 64) __attribute__((amdgpu_waves_per_eu
       qfrag[ks] = __builtin_bit_cast(bf16x8, wv);
     }
     for (int cb = 0; cb < c; cb += kGateChunk) {
-      if constexpr (QUEST)
-        gate_scores_mfma<D, true>(qfrag, kbar, H, h, gb0 + cb, min(kGateChunk, c - cb),
-                                  total_blocks, ss, cb, w, lane);
-      else
-        gate_scores_planes<D>(qfrag, kbar3, H, h, gb0 + cb, min(kGateChunk, c - cb),
-                              total_blocks, ss, cb, w, lane);
+      gate_scores_mfma<D, true>(qfrag, kbar, H, h, gb0 + cb, min(kGateChunk, c - cb),
+                                total_blocks, ss, cb, w, lane);
     }
     __syncthreads();
   } else {
