@@ -224,10 +224,8 @@ constexpr int kGateChunk = 128;  // past blocks per MFMA scoring step (one 32 x 
 constexpr int kGateChunkValu = 64;  // past blocks per fp32 scoring step
 constexpr int kGateWaves = 4;
 constexpr int kGateRowsPerWave = kGateRows / kGateWaves;
-// the single-span kernel: 64 query tokens and 8 waves per workgroup.  Mean
-// gate: wave w scores block tile w for all 64 tokens.  Min/max gate: the two
-// waves of a block tile (one per 32 tokens) read the same pooled-key lines
-// together, so the second read is served by the CU's L1
+// the single-span kernel: 64 query tokens and 8 waves per workgroup; wave w
+// scores block tile w for all 64 tokens
 constexpr int kSpanWaves = 8;
 constexpr int kSpanRows = kSpanWaves * kGateRowsPerWave;
 
@@ -430,6 +428,99 @@ __device__ __forceinline__ void gate_scores_span(const uint16_t* __restrict__ q,
               __builtin_bit_cast(bf16x8, b[t][kk]), acc[t], 0, 0, 0);
   }
   // acc[t][r] = score of block 32 w + 8 (r / 4) + 4 hf + (r % 4) for token 32 t + lane & 31
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int jb = 32 * w + 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ss[32 * t + l32][gate_col(jb)] = jb < nb ? acc[t][r] : -INFINITY;
+  }
+}
+
+// The same tile for the min/max gate: the A rows are the fp32 [kmax, kmin]
+// rows of the blocks, the B columns q+ (against kmax) and q- (against kmin).
+// Each fragment is split into its three exact bf16 terms as in
+// gate_scores_mfma, in the same summation order; when every element of a
+// wave's fragment is a bf16 value (always, for keys pooled from bf16 inputs)
+// the mid and lo terms are zero and their products are skipped.
+template <int D>
+__device__ __forceinline__ void gate_scores_span_minmax(const uint16_t* __restrict__ q, int start,
+                                                        int len, int p0, int H, int h,
+                                                        const float* __restrict__ kmm, int gblk0,
+                                                        int nb, int total_blocks,
+                                                        float (*ss)[kGateStride], int w,
+                                                        int lane) {
+  constexpr int KD = 2 * D;  // length of a [kmax, kmin] row
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int j = 32 * w + l32;
+  const bool ok = j < nb && gblk0 + j < total_blocks;
+  const float* kp = kmm + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * KD + 8 * hf;
+  const uint16_t* qp[2];
+  bool qv[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tok = p0 + 32 * t + l32;
+    qv[t] = tok < len;
+    qp[t] = q + ((size_t)(start + (qv[t] ? tok : p0)) * H + h) * D + 8 * hf;
+  }
+  f32x16 acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  constexpr int KH = D / 64;  // k-steps per group of loads in flight together
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int half = 0; half < KD / (16 * KH); ++half) {
+    f32x4 xa[KH], xb[KH];
+    u32x4 b[2][KH];
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const int ks = half * KH + kk;
+      xa[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * ks);
+      xb[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * ks + 4);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        b[t][kk] = qv[t] ? *reinterpret_cast<const u32x4*>(qp[t] + 16 * (ks % (D / 16))) : zero;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const int ks = half * KH + kk;
+      const f32x4 x0 = ok ? xa[kk] : fzero, x1 = ok ? xb[kk] : fzero;
+      bf16x8 qb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        qb[t] = ks < D / 16 ? sign_part<false>(__builtin_bit_cast(bf16x8, b[t][kk]))
+                            : sign_part<true>(__builtin_bit_cast(bf16x8, b[t][kk]));
+      bf16x8 hi;
+      bool exact = true;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
+        exact = exact && __uint_as_float(hb) == x;
+        hi[e] = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qb[t], acc[t], 0, 0, 0);
+      if (__ballot(!exact) != 0ull) {
+        bf16x8 mid, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 a, bb, cc;
+          split3(e < 4 ? x0[e] : x1[e - 4], a, bb, cc);
+          mid[e] = bb;
+          lo[e] = cc;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qb[t], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qb[t], acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int jb = 32 * w + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -777,27 +868,15 @@ __global__ __launch_bounds__(kSpanWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     return;
   }
-  if constexpr (kMfma && !QUEST) {
+  if constexpr (kMfma) {
     static_assert(32 * kSpanWaves == kGateSpan, "one 32-block tile per wave covers the span");
-    if (32 * w < c)
-      gate_scores_span<D>((const uint16_t*)q, start, len, p0, H, h, kbar3, gb0, c, total_blocks,
-                          ss, w, lane);
-    __syncthreads();
-  } else if constexpr (kMfma) {
-    bf16x8 qfrag[D / 16];
-    const int tok = p0 + 32 * (w >> 2) + (lane & 31);
-    const bool qv = tok < len;
-    const uint16_t* qp = (const uint16_t*)q + ((size_t)(start + (qv ? tok : p0)) * H + h) * D +
-                         8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (qv) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      qfrag[ks] = __builtin_bit_cast(bf16x8, wv);
-    }
-    for (int cb = 0; cb < c; cb += kGateChunk) {
-      gate_scores_mfma<D, true>(qfrag, kbar, H, h, gb0 + cb, min(kGateChunk, c - cb),
-                                total_blocks, ss, cb, w, lane);
+    if (32 * w < c) {
+      if constexpr (QUEST)
+        gate_scores_span_minmax<D>((const uint16_t*)q, start, len, p0, H, h, kbar, gb0, c,
+                                   total_blocks, ss, w, lane);
+      else
+        gate_scores_span<D>((const uint16_t*)q, start, len, p0, H, h, kbar3, gb0, c,
+                            total_blocks, ss, w, lane);
     }
     __syncthreads();
   } else {
@@ -833,7 +912,7 @@ __global__ __launch_bounds__(kSpanWaves * 64) __attribute__((amdgpu_waves_per_eu
 // paths below); among keys equal to the threshold the lower block indices
 // win.
 template <typename T, int D, bool QUEST>
-__global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu(QUEST && D > 64 ? 2 : 4))) void gate_topk_kernel(
+__global__ __launch_bounds__(kGateWaves * 64) __attribute__((amdgpu_waves_per_eu(QUEST || D > 64 ? 2 : 4))) void gate_topk_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar, const uint16_t* __restrict__ kbar3,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
     int total_tokens, int total_blocks, int tiles_per_seq, int H, int block_size, int topk,
