@@ -84,6 +84,30 @@ def test_gate_minmax_all_rows(dev, w):
 
 
 @pytest.mark.parametrize("w", [
+    # one selection span with ragged ends (own blocks not a multiple of 32,
+    # a last tile past the sequence end), d 128 and d 64
+    inputs.custom([64 * 200 + 37, 1000], 2, 128, 64, 6, "bf16", name="minmax-f32pool-d128"),
+    inputs.custom([64 * 90 + 20, 333], 2, 64, 64, 9, "bf16", name="minmax-f32pool-d64"),
+], ids=lambda w: w.name)
+def test_gate_minmax_fp32_pooled(dev, w):
+    # bf16 queries against min/max keys pooled from fp32 keys that are not
+    # bf16 values: the gate splits each pooled value into three exact bf16
+    # terms, so the selections still follow the exact scores
+    _say("gate minmax, fp32 pooled keys", w.name, "seed 7")
+    x = inputs.make_inputs(w, device=dev, seed=7)
+    geom = moba.Geometry.make(x["cu_seqlens"], w.block_size, dev)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    k32 = x["k"].float().cpu() + 1e-3 * torch.randn(x["k"].shape, generator=gen)
+    assert bool((k32 != k32.to(torch.bfloat16).float()).any())
+    kmm = moba.moba_pool_minmax(k32.to(dev), geom)
+    idx = moba.moba_gate_topk_minmax(x["q"], kmm, geom, w.topk).cpu().numpy()
+    rows = np.stack(np.meshgrid(np.arange(w.total_tokens), np.arange(w.heads), indexing="ij"),
+                    -1).reshape(-1, 2)
+    _check_minmax_idx(x["q"].float().cpu().numpy(), k32.numpy(), x["cu_seqlens"],
+                      w.block_size, w.topk, idx, rows)
+
+
+@pytest.mark.parametrize("w", [
     inputs.custom([5000, 3192], 4, 128, 512, 4, "bf16", name="minmax-fwd-8k"),
     inputs.custom([6000, 2100], 2, 128, 1024, 3, "bf16", name="minmax-fwd-B1024"),
 ], ids=lambda w: w.name)
