@@ -502,6 +502,19 @@ hipError_t launch_v_transpose(const void* v, const Geo& g, uint32_t* vmax_bits, 
   return hipGetLastError();
 }
 
+// Butterfly steps across the 16 lanes of a merge row as DPP moves (VALU, no
+// LDS round trip): lane ^ 8 is row_ror:8 (a 16-lane row rotated by half),
+// lane ^ 4 quad_perm [3,2,1,0] (lane ^ 3) then row_half_mirror (lane ^ 7),
+// lane ^ 2 and lane ^ 1 one quad_perm each.
+__device__ __forceinline__ float row16_xor(float v, int m) {
+  const int x = __float_as_int(v);
+  if (m == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
+  if (m == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+  if (m == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+  const int y = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------------------
 // merge: 16 lanes per (token, head) row, 16 rows per workgroup.  Each lane
 // owns D/16 consecutive output dims; the part weights exp(lse_p - lse) go
@@ -547,11 +560,13 @@ __global__ __launch_bounds__(256) void merge_kernel(
       mx = fmaxf(mx, l4[u]);
       if (i < 64) slots[r16][i] = slot;
     }
-    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, row16_xor(mx, o));
     float sum = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) sum += (li + 16 * u < nparts) ? expf(l4[u] - mx) : 0.f;
-    for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 16);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) sum += row16_xor(sum, o);
     tot = mx + logf(sum);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
