@@ -127,8 +127,13 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
   }
 }
 
-// min/max pool: kmm[gb, h, 0, :] = elementwise max of the block's keys,
-// kmm[gb, h, 1, :] = elementwise min (exact: no rounding)
+// min/max pool: the elementwise max and min of the block's keys (exact: no
+// rounding), stored group-major.  The [kmax, kmin] row of (block gb, head h)
+// has 2 D values in 2 D / 4 groups of 4 (groups 0 .. D / 4 - 1 the max,
+// D / 4 .. D / 2 - 1 the min), and group g of every block of head h is one
+// run: kmm[((h * (D / 2) + g) * NB + gb) * 4 + i] = row value 4 g + i.  A
+// gate wave's 32 blocks then read one group as 32 consecutive 16-byte
+// records (512 bytes) instead of 32 separate lines.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_minmax_kernel(
     const T* __restrict__ k, const int32_t* __restrict__ cu_seqlens,
@@ -183,14 +188,25 @@ __global__ __launch_bounds__(256) void pool_minmax_kernel(
     __syncthreads();
   }
   if (ty == 0) {
-    // column col0 + 8 tx + i of the [H * D] row is (head, dim) = divmod(col, D)
+    // column col0 + 8 tx + i of the [H * D] row is (head, dim) = divmod(col, D);
+    // dims e .. e + 7 are the groups e / 4 and e / 4 + 1 of the max half and
+    // D / 4 + e / 4, + 1 of the min half
     const int col = col0 + tx * 8;
     const int h = col / D, e = col - h * D;
-    float* dst = kmm + ((size_t)gb * (hd / D) + h) * 2 * D + e;
+    const size_t nbk = (size_t)gridDim.x;  // total blocks
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      dst[i] = cnt > 0 ? rmax[0][tx * 8 + i] : 0.f;
-      dst[D + i] = cnt > 0 ? rmin[0][tx * 8 + i] : 0.f;
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = half == 0 ? rmax[0][tx * 8 + 4 * gi + i] : rmin[0][tx * 8 + 4 * gi + i];
+          v[i] = cnt > 0 ? x : 0.f;
+        }
+        const int grp = half * (D / 4) + e / 4 + gi;
+        *reinterpret_cast<f32x4*>(kmm + (((size_t)h * (D / 2) + grp) * nbk + gb) * 4) = v;
+      }
     }
   }
 }
@@ -272,7 +288,13 @@ __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
   const bool ok = j < nb && gblk0 + j < total_blocks;
   // lanes past the chunk read block gblk0 (always valid) and zero it, so the
   // loads carry no branch and can all be in flight together
-  const float* kp = kbar + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * KD + 8 * hf;
+  const int blk = ok ? gblk0 + j : gblk0;
+  // mean keys: [NB, H, D] rows; min/max: the group-major layout of
+  // pool_minmax_kernel (groups 4 ks + 2 hf and + 1 hold dims 16 ks + 8 hf .. + 7)
+  const float* kp = QUEST ? kbar + (((size_t)h * (KD / 4) + 2 * hf) * total_blocks + blk) * 4
+                          : kbar + ((size_t)blk * H + h) * KD + 8 * hf;
+  const size_t sa = QUEST ? (size_t)total_blocks * 16 : 16;  // floats per k-step
+  const size_t sb = QUEST ? (size_t)total_blocks * 4 : 4;    // second half of a k-step
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -282,8 +304,8 @@ __device__ __forceinline__ void gate_scores_mfma(const bf16x8 (&qfrag)[D / 16],
   f32x4 xa[KH], xb[KH];
 #pragma unroll
   for (int kk = 0; kk < KH; ++kk) {
-    xa[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * (half * KH + kk));
-    xb[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * (half * KH + kk) + 4);
+    xa[kk] = *reinterpret_cast<const f32x4*>(kp + sa * (half * KH + kk));
+    xb[kk] = *reinterpret_cast<const f32x4*>(kp + sa * (half * KH + kk) + sb);
   }
 #pragma unroll
   for (int kk = 0; kk < KH; ++kk) {
@@ -453,7 +475,11 @@ __device__ __forceinline__ void gate_scores_span_minmax(const uint16_t* __restri
   const int l32 = lane & 31, hf = lane >> 5;
   const int j = 32 * w + l32;
   const bool ok = j < nb && gblk0 + j < total_blocks;
-  const float* kp = kmm + ((size_t)(ok ? gblk0 + j : gblk0) * H + h) * KD + 8 * hf;
+  // dims 16 ks + 8 hf .. + 7 of the block's [kmax, kmin] row: groups
+  // 4 ks + 2 hf and 4 ks + 2 hf + 1 (consecutive lanes read consecutive
+  // 16-byte records of one group)
+  const float* kp = kmm + (((size_t)h * (KD / 4) + 2 * hf) * total_blocks + (ok ? gblk0 + j : gblk0)) * 4;
+  const size_t gstep = (size_t)total_blocks * 4;  // floats between groups
   const uint16_t* qp[2];
   bool qv[2];
 #pragma unroll
@@ -477,8 +503,8 @@ __device__ __forceinline__ void gate_scores_span_minmax(const uint16_t* __restri
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int ks = half * KH + kk;
-      xa[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * ks);
-      xb[kk] = *reinterpret_cast<const f32x4*>(kp + 16 * ks + 4);
+      xa[kk] = *reinterpret_cast<const f32x4*>(kp + 4 * ks * gstep);
+      xb[kk] = *reinterpret_cast<const f32x4*>(kp + (4 * ks + 1) * gstep);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         b[t][kk] = qv[t] ? *reinterpret_cast<const u32x4*>(qp[t] + 16 * (ks % (D / 16))) : zero;

@@ -28,7 +28,7 @@ MOBA_ERR_HIP = -4
 MOBA_F32 = 0
 MOBA_BF16 = 1
 # the MOBA_API_VERSION of include/moba.h these bindings are written for
-API_VERSION = 5
+API_VERSION = 6
 
 EXPORTS = ["moba_api_version", "moba_status_str", "moba_last_hip_error", "moba_pool_keys",
            "moba_gate_topk", "moba_pool_minmax", "moba_gate_topk_minmax", "moba_static_select",
@@ -218,13 +218,23 @@ def moba_gate_topk(q, pooled, geom, topk, block_idx=None, stream=None):
 
 
 def moba_pool_minmax(k, geom, kminmax=None, stream=None):
-    """Elementwise block max and min of the keys: kminmax [NB, H, 2, d] fp32."""
+    """Elementwise block max and min of the keys, exact, in the library's
+    group-major layout: kminmax [H, d / 2, NB, 4] fp32, where group g of a
+    block's [kmax, kmin] row (2d values) holds its values 4g .. 4g + 3
+    (``kminmax_rows`` gives them as [NB, H, 2, d])."""
     H, d = _qkv_shape(k, geom)
     if kminmax is None:
-        kminmax = torch.empty((geom.total_blocks, H, 2, d), dtype=torch.float32, device=k.device)
+        kminmax = torch.empty((H, d // 2, geom.total_blocks, 4), dtype=torch.float32,
+                              device=k.device)
     _check("moba_pool_minmax", lib().moba_pool_minmax(
         _ptr(k), _dtype_code(k.dtype), *geom.args(H, d), _ptr(kminmax), _stream(stream)))
     return kminmax
+
+
+def kminmax_rows(kminmax, num_heads, head_dim, total_blocks):
+    """[NB, H, 2, d] view order (max, then min) of a kminmax buffer (a copy)."""
+    t = kminmax.reshape(num_heads, 2, head_dim // 4, total_blocks, 4)
+    return t.permute(3, 0, 1, 2, 4).reshape(total_blocks, num_heads, 2, head_dim)
 
 
 def moba_gate_topk_minmax(q, kminmax, geom, topk, block_idx=None, stream=None):

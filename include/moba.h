@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOBA_API_VERSION 5
+#define MOBA_API_VERSION 6
 
 /* Size of the device workspace moba_attn_fwd_static keeps inside the library
  * (per GPU, for the life of the process). */
@@ -146,10 +146,15 @@ moba_status moba_gate_topk(const void* q, int dtype, const float* kbar,
  * gate below).  "MoBA: Mixture of Block Attention for Long-Context LLMs"
  * (research.elamur.ai), "Key points": Quest reads as MoBA with smaller blocks
  * and min/max pooling.
- *   kminmax[b, h, 0, :] = elementwise max of k[t, h, :] over the tokens t of
- *   block b;  kminmax[b, h, 1, :] = elementwise min.  Exact (no rounding).
+ *   kmax[b, h, :] = elementwise max of k[t, h, :] over the tokens t of
+ *   block b;  kmin[b, h, :] = elementwise min.  Exact (no rounding).
  *   k        [total_tokens, num_heads, head_dim], dtype
- *   kminmax  [total_blocks, num_heads, 2, head_dim] fp32, written in full
+ *   kminmax  num_heads * total_blocks * 2 * head_dim fp32, written in full,
+ *            group-major: with r = [kmax[b, h, :], kmin[b, h, :]] (2 head_dim
+ *            values) and G = head_dim / 2 groups of 4 per row,
+ *            kminmax[((h * G + g) * total_blocks + b) * 4 + i] = r[4 g + i],
+ *            i.e. a [num_heads, G, total_blocks, 4] array, so that the gate
+ *            reads one group of consecutive blocks as one contiguous run
  */
 moba_status moba_pool_minmax(const void* k, int dtype, const int32_t* cu_seqlens,
                              const int32_t* cu_blocks, int num_seqs, int total_tokens,

@@ -143,6 +143,22 @@ def test_hybrid_schedule():
         moba.layer_forward("sparse", None, None, None, None, 3, 0.1)
 
 
+def test_kminmax_rows_follows_the_header_layout():
+    # the group-major kminmax layout as include/moba.h states it, written out
+    # element by element, read back by the binding's [NB, H, 2, d] view
+    NB, H, d = 5, 3, 8
+    G = d // 2
+    rows = torch.arange(NB * H * 2 * d, dtype=torch.float32).reshape(NB, H, 2, d)
+    buf = torch.empty(H * G * NB * 4, dtype=torch.float32)
+    for b in range(NB):
+        for h in range(H):
+            r = torch.cat([rows[b, h, 0], rows[b, h, 1]])
+            for g in range(G):
+                for i in range(4):
+                    buf[((h * G + g) * NB + b) * 4 + i] = r[4 * g + i]
+    assert torch.equal(moba.kminmax_rows(buf, H, d, NB), rows)
+
+
 def test_probe_arguments(L):
     E = moba.MOBA_ERR_INVALID_ARG
     assert L.moba_probe_mfma_rate(0, 10, 0, FAKE, None) == E
