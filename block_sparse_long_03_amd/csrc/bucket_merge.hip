@@ -77,17 +77,82 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
       for (int j = 0; j < topk; ++j) visit(row[j]);
     }
   };
-  for (int r = threadIdx.x; r < nrows; r += 256)
-    walk(r, [&](int h, int e) {
-      if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
-      else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
-    });
+  auto add = [&](int h, int e) {
+    if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
+    else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
+  };
+  constexpr int kCK = 16, kRB = 4;
+  if ((topk & 3) == 0 && topk <= kCK) {
+    // kRB rows per thread at a time, all their loads issued before any of
+    // them is walked, so that a thread has kRB rows in flight instead of one
+    for (int r0 = threadIdx.x; r0 < nrows; r0 += 256 * kRB) {
+      int4 e4[kRB][kCK / 4];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int r = min(r0 + 256 * u, nrows - 1);  // rows past the end: loaded, not walked
+        const int p = p0 + r / HC, h = r - (r / HC) * HC;
+        const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * topk;
+#pragma unroll
+        for (int j = 0; j < kCK / 4; ++j)
+          e4[u][j] = 4 * j < topk ? *reinterpret_cast<const int4*>(row + 4 * j)
+                                  : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int r = r0 + 256 * u;
+        if (r >= nrows) break;
+        const int p = p0 + r / HC, h = r - (r / HC) * HC;
+        const int c = p / block_size;
+        int ev[kCK];
+#pragma unroll
+        for (int j = 0; j < kCK / 4; ++j) {
+          ev[4 * j] = e4[u][j].x;
+          ev[4 * j + 1] = e4[u][j].y;
+          ev[4 * j + 2] = e4[u][j].z;
+          ev[4 * j + 3] = e4[u][j].w;
+        }
+        // the accepted historical entries (accept_hist), as walk visits them
+        uint32_t accm = 0u;
+        int last = -1, nh = 0;
+#pragma unroll
+        for (int q = 0; q < kCK; ++q)
+          if (q < topk && accept_hist(ev[q], c, last, nh, topk)) {
+            accm |= 1u << q;
+            last = ev[q];
+            ++nh;
+          }
+        if (c < dense_blocks) {
+          if (nh == c) continue;  // a dense-prefix row (dense_row)
+          if (gb0 + c < NB) notfull[(size_t)h * NB + gb0 + c] = 1;
+        }
+#pragma unroll
+        for (int q = 0; q < kCK; ++q)
+          if (((accm >> q) & 1u) && gb0 + ev[q] < NB) add(h, ev[q]);
+      }
+    }
+  } else {
+    for (int r = threadIdx.x; r < nrows; r += 256) walk(r, add);
+  }
   if (!use_lds) return;
   __syncthreads();
   for (int b = threadIdx.x; b < nbins * HC; b += 256) {
     const int h = b / nbins, e = b - (b / nbins) * nbins;
     if (hist[b]) atomicAdd(&counts[(size_t)h * NB + gb0 + e], hist[b]);
   }
+}
+
+// Inclusive sum over the 64 lanes of a wave with DPP adds: row_shr 1, 2, 4, 8
+// (zero from outside the 16-lane row) scan each row, then row_bcast:15 adds
+// row 0's (row 2's) total to row 1 (row 3) and row_bcast:31 adds the total
+// of lanes 0..31 to rows 2 and 3; the rows left out keep 0 (the old value).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
 }
 
 // Scatter of one head's entries of a token tile into the per-(head, block)
@@ -245,14 +310,9 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     for (int b0 = 0; b0 < nbins; b0 += 64) {
       const int b = b0 + lane;
       const int v = b < nbins ? hist[b] : 0;
-      int inc = v;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(inc, d);
-        if (lane >= d) inc += u;
-      }
+      const int inc = wave_incl_scan(v);
       if (b < nbins) loff[b] = carry + inc - v;
-      carry += __shfl(inc, 63);
+      carry += __builtin_amdgcn_readlane(inc, 63);
     }
     if (lane == 0) loff[nbins] = carry;
   }
