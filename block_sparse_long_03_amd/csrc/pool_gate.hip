@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
 template <typename T>
 __global__ __launch_bounds__(256) void pool_minmax_kernel(
     const T* __restrict__ k, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int hd, int D,
-    int block_size, float* __restrict__ kmm) {
+    const int32_t* __restrict__ cu_blocks, int num_seqs, int total_tokens, int total_blocks,
+    int hd, int D, int block_size, float* __restrict__ kmm) {
   __shared__ float rmax[32][65];
   __shared__ float rmin[32][65];
   const int gb = blockIdx.x;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void pool_minmax_kernel(
     // D / 4 + e / 4, + 1 of the min half
     const int col = col0 + tx * 8;
     const int h = col / D, e = col - h * D;
-    const size_t nbk = (size_t)gridDim.x;  // total blocks
+    const size_t nbk = (size_t)total_blocks;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -1284,11 +1284,11 @@ hipError_t launch_pool_minmax(const void* k, bool bf16, const Geo& g, float* kmm
   if (bf16)
     hipLaunchKernelGGL(pool_minmax_kernel<uint16_t>, grid, dim3(256), 0, st,
                        (const uint16_t*)k, g.cu_seqlens, g.cu_blocks, g.num_seqs,
-                       g.total_tokens, hd, g.head_dim, g.block_size, kmm);
+                       g.total_tokens, g.total_blocks, hd, g.head_dim, g.block_size, kmm);
   else
     hipLaunchKernelGGL(pool_minmax_kernel<float>, grid, dim3(256), 0, st, (const float*)k,
-                       g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, hd, g.head_dim,
-                       g.block_size, kmm);
+                       g.cu_seqlens, g.cu_blocks, g.num_seqs, g.total_tokens, g.total_blocks,
+                       hd, g.head_dim, g.block_size, kmm);
   return hipGetLastError();
 }
 
