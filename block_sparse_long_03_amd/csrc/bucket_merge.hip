@@ -8,6 +8,8 @@
 // log-sum-exp values lse_p and normalised outputs o_p,
 //   lse = ln sum_p exp(lse_p),  o = sum_p exp(lse_p - lse) o_p,
 // an exact identity for softmax over the union of the parts' keys.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -81,21 +83,21 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     if (use_lds) atomicAdd(&hist[h * nbins + e], 1);
     else atomicAdd(&counts[(size_t)h * NB + gb0 + e], 1);
   };
-  constexpr int kCK = 16, kRB = 4;
-  if ((topk & 3) == 0 && topk <= kCK) {
-    // kRB rows per thread at a time, all their loads issued before any of
-    // them is walked, so that a thread has kRB rows in flight instead of one
+  // kRB rows per thread at a time, all their loads issued before any of them
+  // is walked, so that a thread has kRB rows in flight instead of one; the
+  // row width KC = topk is a compile-time constant of the walk
+  constexpr int kRB = 4;
+  auto batched = [&](auto kc_t) {
+    constexpr int KC = decltype(kc_t)::value;
     for (int r0 = threadIdx.x; r0 < nrows; r0 += 256 * kRB) {
-      int4 e4[kRB][kCK / 4];
+      int4 e4[kRB][KC / 4];
 #pragma unroll
       for (int u = 0; u < kRB; ++u) {
         const int r = min(r0 + 256 * u, nrows - 1);  // rows past the end: loaded, not walked
         const int p = p0 + r / HC, h = r - (r / HC) * HC;
-        const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * topk;
+        const int32_t* row = block_idx + ((size_t)(start + p) * H + h0 + h) * KC;
 #pragma unroll
-        for (int j = 0; j < kCK / 4; ++j)
-          e4[u][j] = 4 * j < topk ? *reinterpret_cast<const int4*>(row + 4 * j)
-                                  : make_int4(-1, -1, -1, -1);
+        for (int j = 0; j < KC / 4; ++j) e4[u][j] = *reinterpret_cast<const int4*>(row + 4 * j);
       }
 #pragma unroll
       for (int u = 0; u < kRB; ++u) {
@@ -103,9 +105,9 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
         if (r >= nrows) break;
         const int p = p0 + r / HC, h = r - (r / HC) * HC;
         const int c = p / block_size;
-        int ev[kCK];
+        int ev[KC];
 #pragma unroll
-        for (int j = 0; j < kCK / 4; ++j) {
+        for (int j = 0; j < KC / 4; ++j) {
           ev[4 * j] = e4[u][j].x;
           ev[4 * j + 1] = e4[u][j].y;
           ev[4 * j + 2] = e4[u][j].z;
@@ -115,8 +117,8 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
         uint32_t accm = 0u;
         int last = -1, nh = 0;
 #pragma unroll
-        for (int q = 0; q < kCK; ++q)
-          if (q < topk && accept_hist(ev[q], c, last, nh, topk)) {
+        for (int q = 0; q < KC; ++q)
+          if (accept_hist(ev[q], c, last, nh, KC)) {
             accm |= 1u << q;
             last = ev[q];
             ++nh;
@@ -126,12 +128,18 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
           if (gb0 + c < NB) notfull[(size_t)h * NB + gb0 + c] = 1;
         }
 #pragma unroll
-        for (int q = 0; q < kCK; ++q)
+        for (int q = 0; q < KC; ++q)
           if (((accm >> q) & 1u) && gb0 + ev[q] < NB) add(h, ev[q]);
       }
     }
-  } else {
-    for (int r = threadIdx.x; r < nrows; r += 256) walk(r, add);
+  };
+  switch (topk) {
+    case 4: batched(std::integral_constant<int, 4>()); break;
+    case 8: batched(std::integral_constant<int, 8>()); break;
+    case 12: batched(std::integral_constant<int, 12>()); break;
+    case 16: batched(std::integral_constant<int, 16>()); break;
+    default:
+      for (int r = threadIdx.x; r < nrows; r += 256) walk(r, add);
   }
   if (!use_lds) return;
   __syncthreads();
@@ -317,12 +325,22 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
     if (lane == 0) loff[nbins] = carry;
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nbins; b += kScatterThreads) {
-    const int n = hist[b];
-    gbase[b] = n ? offsets[key0 + b] + atomicAdd(&counts[key0 + b], n) : 0;
-    hist[b] = 0;
+  // each block's range of the list (one bin per thread: nbins <= kScatterBins
+  // <= kScatterThreads): the reservation is issued here and its result used
+  // only after the staging, behind a barrier that waits for LDS alone, so
+  // the atomic's round trip overlaps the staging
+  static_assert(kScatterBins <= kScatterThreads, "one bin per thread");
+  const int bme = threadIdx.x;
+  int n_me = 0, off_me = 0, res_me = 0;
+  if (bme < nbins) {
+    n_me = hist[bme];
+    hist[bme] = 0;
+    if (n_me) {
+      off_me = offsets[key0 + bme];
+      res_me = atomicAdd(&counts[key0 + bme], n_me);
+    }
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (cached) {
 #pragma unroll
     for (int q = 0; q < kCacheK; ++q)
@@ -335,6 +353,7 @@ __global__ __launch_bounds__(kScatterThreads) void bucket_scatter_kernel(
         stage[loff[e] + atomicAdd(&hist[e], 1)] = value(slot, pp);
       });
   }
+  if (bme < nbins) gbase[bme] = n_me ? off_me + res_me : 0;
   __syncthreads();
   // each wave copies whole runs: lanes write consecutive list entries
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
