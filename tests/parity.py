@@ -118,3 +118,20 @@ def check_idx_all_rows(q, k, cu, B, topk, idx, heads=None):
     st = dict(n_near=n_near, n_mismatch=n_mis, rows=int(T) * (H if heads is None else len(heads)))
     emit(st)
     return st
+
+
+def check_idx_rows(q, k, cu, B, topk, idx, rows):
+    """Selections of the given (global token, head) rows, head by head."""
+    n_near = n_mis = 0
+    for h in np.unique(rows[:, 1]):
+        th = rows[rows[:, 1] == h, 0]
+        rows_h = np.stack([th, np.zeros_like(th)], axis=1)
+        q_h, k_h = host_head(q, int(h)), host_head(k, int(h))
+        tt = torch.as_tensor(th, device=idx.device)
+        idx_g = idx[tt, int(h), :].cpu().numpy().astype(np.int64)
+        sel = check_selection(q_h, k_h, cu, B, topk, rows_h, idx_g)
+        n_near += sel["n_near"]
+        n_mis += sel["n_mismatch"]
+    st = dict(n_near=n_near, n_mismatch=n_mis, rows=len(rows))
+    emit(st)
+    return st

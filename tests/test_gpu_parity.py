@@ -191,8 +191,9 @@ def test_moba_sampled(dev, name, per_head, heads, sel_heads):
 def test_moba_1m_sampled(dev):
     """The 1M-token workload in the launch configuration bench.py times:
     outputs on 2048 seeded rows (8 heads), selections on every row of two
-    heads, and causal validity of every selection row; then the same
-    attention in passes of 8 heads, which must reproduce it bit for bit."""
+    heads and on 4096 seeded rows of every head, and causal validity of
+    every selection row; then the same attention in passes of 8 heads,
+    which must reproduce it bit for bit."""
     w = inputs.WORKLOADS["1m"]
     x, geom, out, lse, idx = _run(w, dev)
     rows = inputs.sample_rows(w, 256, heads=[0, 3, 9, 14, 17, 22, 28, 31])
@@ -202,6 +203,10 @@ def test_moba_1m_sampled(dev):
     st = parity.check_idx_all_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx,
                                    heads=[5, 26])
     print("1m heads 5, 26 selections", st)
+    _say("1m: selections of 4096 seeded rows of every head")
+    st = parity.check_idx_rows(x["q"], x["k"], x["cu_seqlens"], w.block_size, w.topk, idx,
+                               inputs.sample_rows(w, 4096))
+    print("1m 4096 rows x 32 heads selections", st)
     _check_rows_valid(w, idx, out, lse)
     _say("1m: attention again in passes of 8 heads")
     torch.cuda.empty_cache()
